@@ -1,0 +1,209 @@
+"""Throughput of one paged-attention step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+A step is the whole hot path over one batch of synthetic input: the cache
+scatter of the step's new K/V (pa_reshape_and_cache) followed by attention of
+every query row over its paged context (pa_attention: plan, chunk/row-wise
+kernels, split-K merge).  Inputs are resident in HBM before the timed region.
+Small configurations rotate over several identical replicas placed in
+different memory, so that no step finds its K/V in the 256 MB last-level
+cache left over from the step before.
+
+Prints one JSON line.  The default workload is the decode-only bf16 step
+(64 sequences x 1 query token, cached contexts uniform in [512, 2048], 32 query
+/ 8 KV heads, head_dim 128, 16-token blocks, 16384-block pool).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode KV-read GB/s (% HBM peak); prefill/mixed TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def workload_desc(spec) -> str:
+    kinds = {1: "tiny fp32 step: 17-token prefill + decodes over 5 and 33 cached tokens",
+             2: "decode-only bf16: 64 seqs x 1 token, context U[512,2048]",
+             3: "chunked-prefill bf16: 8 x 512-token chunks over context 0/512/1024/1536",
+             4: "mixed bf16, 8192-token budget: 4 x 512-token chunks + 6144 decodes (context U[1024,8192])",
+             5: "long-context + prefix-shared decode bf16: 256 decodes sharing 128 blocks + 16 at 64k-128k"}
+    return (f"{kinds.get(spec.cfg_id, spec.name)}; Hq={spec.num_q_heads} Hkv={spec.num_kv_heads} "
+            f"D={spec.head_dim} block=16 pool={spec.num_blocks} blocks")
+
+
+def _unique_tokens(spec, reqs):
+    """Physical K/V tokens a set of requests reads: a shared prefix counts once."""
+    sharers = sum(1 for r in reqs if r.shares_prefix)
+    return sum(r.seq_len for r in reqs) - spec.prefix_tokens * max(0, sharers - 1)
+
+
+def algorithmic_work(spec, mfma_rows: bool):
+    """Bytes and FLOPs the method itself must move / compute in one step.
+
+    K/V bytes count each physical token once per step (kv heads read once, not per
+    query head); causal FLOPs count only unmasked (query, key) pairs, 2 for QK^T and
+    2 for PV per pair per query head."""
+    elt, hkv, hq, d = spec.elt_bytes, spec.num_kv_heads, spec.num_q_heads, spec.head_dim
+    kv_tok = 2 * hkv * d * elt
+    row_reqs = [r for r in spec.requests if r.query == 1 or (r.query > 1 and not mfma_rows)]
+    chunk_reqs = [r for r in spec.requests if r.query > 1 and mfma_rows]
+    pair_flops = lambda r: 4 * d * hq * (r.query * r.context + r.query * (r.query + 1) // 2)
+    rows = sum(r.query for r in row_reqs)
+    decode_bytes = (_unique_tokens(spec, row_reqs) * kv_tok + rows * hq * d * (elt + 4)
+                    + sum(-(-r.seq_len // 16) for r in row_reqs) * 4)
+    return dict(kv_unique_bytes=_unique_tokens(spec, spec.requests) * kv_tok,
+                kv_logical_bytes=sum(r.seq_len for r in spec.requests) * kv_tok,
+                decode_kernel_bytes=decode_bytes,
+                causal_flops=sum(pair_flops(r) for r in spec.requests),
+                chunk_flops=sum(pair_flops(r) for r in chunk_reqs),
+                reshape_bytes=spec.num_tokens * (2 * kv_tok + 4))
+
+
+def cpu_baseline(spec, seconds: float):
+    """The fp64 oracle timed on this host's cores over a bounded sample of the workload."""
+    import numpy as np
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import workloads as W
+    from oracle import as_f64, causal_attention
+    from oracle_data import bits
+
+    cores = len(os.sched_getaffinity(0))
+    kv_tok = 2 * spec.num_kv_heads * spec.head_dim * spec.elt_bytes
+    order = list(range(spec.num_seqs))
+    if spec.cfg_id == 4:
+        order = list(range(4)) + list(np.random.default_rng(0).choice(np.arange(4, spec.num_seqs), 256, replace=False))
+    if spec.cfg_id == 5:
+        order = list(range(32)) + [256, 257]
+    prepared = []
+    for i in order:
+        r = spec.requests[i]
+        q = as_f64(bits(W.q_values(spec, r)), spec.dtype)
+        K = as_f64(bits(W.kv_values(spec, "k", r, 0, r.seq_len)), spec.dtype)
+        V = as_f64(bits(W.kv_values(spec, "v", r, 0, r.seq_len)), spec.dtype)
+        prepared.append((r, q, K, V))
+    done_bytes = done_flops = 0
+    n_seq = 0
+    t0 = time.perf_counter()
+    while True:
+        for r, q, K, V in prepared:
+            causal_attention(q, K, V, r.context + np.arange(r.query), spec.scale)
+            done_bytes += r.seq_len * kv_tok
+            done_flops += 4 * spec.head_dim * spec.num_q_heads * (r.query * r.context + r.query * (r.query + 1) // 2)
+            n_seq += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return dict(bytes_per_s=done_bytes / dt, flops_per_s=done_flops / dt, cores=cores,
+                sample=f"{n_seq} sequence passes of the oracle (numpy float64) over {len(prepared)} "
+                       f"sequences of this workload, {dt:.1f} s of host compute")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--replicas", type=int, default=0, help="input replicas to rotate over (0: auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the step shards by sequence or kv head with no exchange; see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_kv_varlen_reshape_amd as pk
+    import workloads as W
+    from workloads.device import build_device_step
+
+    torch.cuda.set_device(0)
+    spec = W.make_config(args.config)
+    pool_bytes = 2 * spec.num_blocks * spec.num_kv_heads * 16 * spec.head_dim * spec.elt_bytes
+    reps = args.replicas or max(1, min(8, int((1 << 30) // max(1, pool_bytes)) + 1))
+    if args.config in (4, 5):
+        reps = 1
+    steps = [build_device_step(spec, device="cuda:0") for _ in range(reps)]
+    outs = [torch.empty((spec.num_tokens, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device="cuda:0")
+            for _ in range(reps)]
+    wss = [s.workspace() for s in steps]
+    torch.cuda.synchronize()
+
+    def step(i):
+        s = steps[i % reps]
+        s.reshape()
+        s.attention(out=outs[i % reps], workspace=wss[i % reps])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    pk.pa_profile_enable((1 << pk.PA_K_DECODE) | (1 << pk.PA_K_CHUNK))
+    pk.pa_profile_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    prof = pk.pa_profile_read()
+    pk.pa_profile_enable(0)
+
+    use_mfma = spec.dtype == "bf16" and pk.pa_get_option(pk.PA_OPT_FORCE_ROWWISE) == 0 and prof["chunk_mfma"][0] > 0
+    work = algorithmic_work(spec, use_mfma)
+    ms = dt * 1e3 / args.steps
+    decode_n, decode_ms = prof["decode_splitk"]
+    chunk_n, chunk_ms = prof["chunk_mfma"]
+    decode_avg = decode_ms / decode_n if decode_n else float("nan")
+    chunk_avg = chunk_ms / chunk_n if chunk_n else float("nan")
+
+    prefill_like = args.config == 3
+    if prefill_like:
+        value = work["causal_flops"] / (ms * 1e-3) / 1e12
+        unit = "TFLOP/s"
+    else:
+        value = work["kv_unique_bytes"] / (ms * 1e-3) / 1e9
+        unit = "GB/s"
+    if use_mfma and prefill_like:
+        ach = work["chunk_flops"] / (chunk_avg * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=ach, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=ach / MFMA_BF16_PEAK_TFLOPS, traffic=None, kernel="chunk_mfma",
+                    kernel_avg_us=chunk_avg * 1e3)
+    else:
+        ach = work["decode_kernel_bytes"] / (decode_avg * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS,
+                    traffic=None, kernel="decode_splitk", kernel_avg_us=decode_avg * 1e3)
+    res = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": spec.dtype, "data": "synthetic",
+        "config": {"workload": workload_desc(spec), "num_seqs": spec.num_seqs, "num_tokens": spec.num_tokens,
+                   "kv_unique_bytes": work["kv_unique_bytes"], "kv_logical_bytes": work["kv_logical_bytes"],
+                   "causal_flops": work["causal_flops"], "replicas": reps},
+        "roofline": roof,
+        "kernels_avg_us": {"decode_splitk": decode_avg * 1e3, "chunk_mfma": chunk_avg * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(spec, args.cpu_seconds)
+        res["cpu_baseline"] = {"value": cb["flops_per_s"] / 1e12 if prefill_like else cb["bytes_per_s"] / 1e9,
+                               "unit": unit, "cores": cb["cores"], "kind": "oracle", "sample": cb["sample"]}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,280 @@
+// C-ABI entry points of libpa: argument checks, workspace layout and the
+// launch sequence of one step (scatter; plan -> chunk -> row-wise -> reduce).
+#include <atomic>
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "internal.h"
+
+namespace pa {
+
+int device_cus() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> g(mu);
+  if (dev >= int(cache.size())) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+namespace {
+
+// ---------------------------------------------------------------- kernel timing
+std::mutex g_prof_mu;
+std::atomic<int32_t> g_prof_mask{0};
+struct Timed {
+  int kind;
+  hipEvent_t start, stop;
+};
+std::vector<Timed> g_pending;
+std::vector<hipEvent_t> g_spare;
+
+hipEvent_t take_event() {
+  hipEvent_t e = nullptr;
+  {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    if (!g_spare.empty()) {
+      e = g_spare.back();
+      g_spare.pop_back();
+    }
+  }
+  if (!e && hipEventCreate(&e) != hipSuccess) e = nullptr;
+  return e;
+}
+
+}  // namespace
+
+KernelTimer::KernelTimer(int kind, hipStream_t st) : kind_(kind), st_(st) {
+  if (!(g_prof_mask.load() & (1 << kind))) return;
+  start_ = take_event();
+  if (start_ && hipEventRecord(start_, st_) != hipSuccess) start_ = nullptr;
+}
+
+KernelTimer::~KernelTimer() {
+  if (!start_) return;
+  hipEvent_t stop = take_event();
+  if (!stop || hipEventRecord(stop, st_) != hipSuccess) return;
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  g_pending.push_back({kind_, start_, stop});
+}
+
+namespace {
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+int64_t target_items() {
+  const int64_t t = option(PA_OPT_TARGET_ITEMS);
+  return t > 0 ? t : kDefaultTargetItems;
+}
+
+int check_dims(int32_t hkv, int32_t d, int32_t bs, int32_t dtype, int64_t nb, const char* who) {
+  if (hkv <= 0) return fail(PA_ERR_INVALID, "%s: num_kv_heads must be positive", who);
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d not supported", who, dtype);
+  if (bs != kBlock) return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only 16 is built)", who, bs);
+  if (d != 64 && d != 128) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128 are built)", who, d);
+  if (nb <= 0 || nb * kBlock >= (int64_t(1) << 31))
+    return fail(PA_ERR_INVALID, "%s: num_blocks %lld out of range", who, (long long)nb);
+  return PA_OK;
+}
+
+}  // namespace
+
+Workspace layout_workspace(const StepShape& s, void* ws) {
+  Workspace w{};
+  const int64_t T = s.num_tokens > 0 ? s.num_tokens : 1;
+  w.rows_cap = T;
+  w.tiles_cap = T;
+  const int64_t fixed = option(PA_OPT_SPLIT_TOKENS);
+  if (fixed > 0) {
+    const int64_t max_keys = int64_t(s.max_blocks_per_seq) * kBlock;
+    w.splits_cap = w.rows_cap * ((max_keys + fixed - 1) / fixed);
+  } else {
+    w.splits_cap = (target_items() + s.num_kv_heads - 1) / s.num_kv_heads + w.rows_cap;
+  }
+  if (w.splits_cap < 1) w.splits_cap = 1;
+  char* p = static_cast<char*>(ws);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* r = p ? p + off : nullptr;
+    off += align_up(bytes);
+    return r;
+  };
+  w.hdr = reinterpret_cast<int32_t*>(take(H_WORDS * sizeof(int32_t)));
+  w.row_tok = reinterpret_cast<int32_t*>(take(w.rows_cap * sizeof(int32_t)));
+  w.row_seq = reinterpret_cast<int32_t*>(take(w.rows_cap * sizeof(int32_t)));
+  w.row_len = reinterpret_cast<int32_t*>(take(w.rows_cap * sizeof(int32_t)));
+  w.split_base = reinterpret_cast<int32_t*>(take((w.rows_cap + 1) * sizeof(int32_t)));
+  w.items = reinterpret_cast<int4*>(take(w.splits_cap * sizeof(int4)));
+  w.reduce = reinterpret_cast<int4*>(take(w.rows_cap * sizeof(int4)));
+  w.tiles = reinterpret_cast<int2*>(take(w.tiles_cap * sizeof(int2)));
+  w.part_o = reinterpret_cast<float*>(take(size_t(w.splits_cap) * s.num_q_heads * s.head_dim * sizeof(float)));
+  w.part_ml = reinterpret_cast<float2*>(take(size_t(w.splits_cap) * s.num_q_heads * sizeof(float2)));
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" int pa_reshape_and_cache(const void* k, const void* v, const int32_t* slot_mapping, void* k_cache,
+                                    void* v_cache, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int64_t num_blocks, int32_t dtype, void* stream) {
+  clear_error();
+  if (int rc = check_dims(num_kv_heads, head_dim, block_size, dtype, num_blocks, "pa_reshape_and_cache")) return rc;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID, "pa_reshape_and_cache: num_tokens < 0");
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return fail(PA_ERR_INVALID, "pa_reshape_and_cache: null pointer");
+  const int32_t row_bytes = head_dim * (dtype == PA_BF16 ? 2 : 4);
+  hipError_t e;
+  {
+    KernelTimer t(PA_K_RESHAPE, static_cast<hipStream_t>(stream));
+    e = launch_reshape_and_cache(k, v, slot_mapping, k_cache, v_cache, num_tokens, num_kv_heads, row_bytes,
+                                 num_blocks, static_cast<hipStream_t>(stream));
+  }
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_reshape_and_cache: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+extern "C" size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq) {
+  if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_blocks_per_seq < 0)
+    return 0;
+  StepShape s{num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq};
+  return layout_workspace(s, nullptr).bytes;
+}
+
+extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            const int32_t* seq_lens, const int32_t* query_start_loc, const int32_t* context_lens,
+                            float scale, float* out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                            int32_t max_blocks_per_seq, int32_t dtype, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  clear_error();
+  if (int rc = check_dims(num_kv_heads, head_dim, block_size, dtype, num_blocks, "pa_attention")) return rc;
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID, "pa_attention: num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  const int group = num_q_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PA_ERR_UNSUPPORTED, "pa_attention: query heads per kv head = %d (1, 2, 4 or 8 are built)", group);
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq < 0)
+    return fail(PA_ERR_INVALID, "pa_attention: negative size");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "pa_attention: scale is not finite");
+  if (num_tokens == 0 || num_seqs == 0) return PA_OK;
+  if (max_blocks_per_seq == 0) return fail(PA_ERR_INVALID, "pa_attention: max_blocks_per_seq is 0 with query rows");
+  if (int64_t(max_blocks_per_seq) * kBlock >= (int64_t(1) << 31))
+    return fail(PA_ERR_INVALID, "pa_attention: max_blocks_per_seq too large");
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !context_lens || !out)
+    return fail(PA_ERR_INVALID, "pa_attention: null pointer");
+  StepShape shape{num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq};
+  const size_t need = layout_workspace(shape, nullptr).bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "pa_attention: workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(PA_ERR_WORKSPACE, "pa_attention: workspace must be 256-byte aligned");
+
+  const Workspace w = layout_workspace(shape, workspace);
+  const bool bf16 = dtype == PA_BF16;
+  const bool use_mfma = !option(PA_OPT_FORCE_ROWWISE) && chunk_supported(head_dim, group, bf16);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  PlanArgs pa_args{};
+  pa_args.qsl = query_start_loc;
+  pa_args.ctx = context_lens;
+  pa_args.num_seqs = num_seqs;
+  pa_args.num_tokens = num_tokens;
+  pa_args.num_kv_heads = num_kv_heads;
+  pa_args.max_len = max_blocks_per_seq * kBlock;
+  pa_args.use_mfma = use_mfma ? 1 : 0;
+  pa_args.fixed_split = int32_t(option(PA_OPT_SPLIT_TOKENS));
+  pa_args.target_items = int32_t(target_items());
+
+  AttnArgs a{};
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.bt = block_tables;
+  a.seq_lens = seq_lens;
+  a.qsl = query_start_loc;
+  a.ctx = context_lens;
+  a.out = out;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.d = head_dim;
+  a.mbps = max_blocks_per_seq;
+  a.nb = num_blocks;
+  a.bf16 = bf16 ? 1 : 0;
+
+  hipError_t e;
+  {
+    KernelTimer t(PA_K_PLAN, st);
+    e = launch_plan(pa_args, w, st);
+  }
+  if (e == hipSuccess && use_mfma) {
+    KernelTimer t(PA_K_CHUNK, st);
+    e = launch_chunk(a, w, group, st);
+  }
+  if (e == hipSuccess) {
+    KernelTimer t(PA_K_DECODE, st);
+    e = launch_decode(a, w, group, st);
+  }
+  if (e == hipSuccess) {
+    KernelTimer t(PA_K_REDUCE, st);
+    e = launch_reduce(a, w, group, st);
+  }
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_attention: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+extern "C" int pa_profile_enable(int32_t mask) {
+  clear_error();
+  if (mask < 0 || mask >= (1 << PA_K_COUNT)) return fail(PA_ERR_INVALID, "pa_profile_enable: bad mask %d", mask);
+  g_prof_mask = mask;
+  return PA_OK;
+}
+
+extern "C" int pa_profile_read(int64_t* counts, double* total_ms) {
+  clear_error();
+  std::vector<Timed> pend;
+  {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    pend.swap(g_pending);
+  }
+  int64_t c[PA_K_COUNT] = {0};
+  double ms[PA_K_COUNT] = {0};
+  int rc = PA_OK;
+  for (const Timed& t : pend) {
+    float x = 0.f;
+    if (hipEventSynchronize(t.stop) == hipSuccess && hipEventElapsedTime(&x, t.start, t.stop) == hipSuccess) {
+      c[t.kind] += 1;
+      ms[t.kind] += x;
+    } else {
+      rc = fail(PA_ERR_HIP, "pa_profile_read: event query failed");
+    }
+  }
+  {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    for (const Timed& t : pend) {
+      g_spare.push_back(t.start);
+      g_spare.push_back(t.stop);
+    }
+  }
+  for (int k = 0; k < PA_K_COUNT; ++k) {
+    if (counts) counts[k] = c[k];
+    if (total_ms) total_ms[k] = ms[k];
+  }
+  return rc;
+}

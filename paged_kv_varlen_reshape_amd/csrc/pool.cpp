@@ -1,0 +1,181 @@
+// Host block allocator: pa_pool_*.
+//
+// Allocation procedure of the Inside vLLM summary (techfeed.io), section
+// "PagedAttentionの仕組み": a request that will hold T tokens needs
+// ceil(T / block_size) blocks; the blocks it lacks are taken from the head of
+// the free-block queue and appended to its list in req_to_blocks.  When the
+// queue is too short the page's engine preempts a lower-priority request;
+// picking that request is scheduler policy, so this allocator reports
+// PA_ERR_NO_BLOCKS and changes nothing.  Blocks go back to the pool when
+// tokens no longer need them (engr-sng explainer of the same article,
+// paragraph on Paging Attention): release drops one reference from each block
+// of the request, in list order, and appends blocks that reach zero references
+// to the tail of the queue.  Prefix caching (Inside vLLM summary, "高度な機能群")
+// shares already cached blocks between requests with one reference each.
+//
+// The free queue is a ring buffer of block ids (capacity num_blocks, since a
+// block is in the queue at most once), so allocation and release are O(blocks
+// moved) with no per-call heap traffic beyond the request's own vector.
+#include <cstring>
+#include <unordered_map>
+#include <vector>
+
+#include "errors.h"
+
+struct pa_pool {
+  int64_t num_blocks;
+  int32_t block_size;
+  std::vector<int32_t> ring;  // free queue storage
+  int64_t head = 0;           // index of the first free block in `ring`
+  int64_t count = 0;          // blocks in the queue
+  std::vector<int32_t> refcount;
+  std::unordered_map<int64_t, std::vector<int32_t>> req_to_blocks;
+
+  int32_t pop_front() {
+    int32_t b = ring[head];
+    head = (head + 1 == num_blocks) ? 0 : head + 1;
+    --count;
+    return b;
+  }
+  void push_back(int32_t b) {
+    int64_t tail = head + count;
+    if (tail >= num_blocks) tail -= num_blocks;
+    ring[tail] = b;
+    ++count;
+  }
+};
+
+extern "C" pa_pool* pa_pool_create(int64_t num_blocks, int32_t block_size, const int32_t* initial_order) {
+  pa::clear_error();
+  if (num_blocks <= 0 || num_blocks > (int64_t(1) << 31) - 1) {
+    pa::fail(PA_ERR_INVALID, "pa_pool_create: num_blocks %lld out of range", (long long)num_blocks);
+    return nullptr;
+  }
+  if (block_size <= 0 || num_blocks * int64_t(block_size) > (int64_t(1) << 31) - 1) {
+    pa::fail(PA_ERR_INVALID, "pa_pool_create: block_size must be positive and slots must fit in int32");
+    return nullptr;
+  }
+  pa_pool* p = new pa_pool;
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->ring.resize(num_blocks);
+  p->refcount.assign(num_blocks, 0);
+  if (initial_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int64_t i = 0; i < num_blocks; ++i) {
+      int32_t b = initial_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete p;
+        pa::fail(PA_ERR_INVALID, "pa_pool_create: initial_order is not a permutation (entry %lld)",
+                 (long long)i);
+        return nullptr;
+      }
+      seen[b] = 1;
+      p->ring[i] = b;
+    }
+  } else {
+    for (int64_t i = 0; i < num_blocks; ++i) p->ring[i] = int32_t(i);
+  }
+  p->count = num_blocks;
+  return p;
+}
+
+extern "C" void pa_pool_destroy(pa_pool* pool) { delete pool; }
+
+extern "C" int pa_allocate_slots(pa_pool* pool, int64_t req, int64_t num_computed, int64_t num_new,
+                                 int32_t* new_ids_out, int32_t cap, int32_t* n_out) {
+  pa::clear_error();
+  if (n_out) *n_out = 0;
+  if (!pool) return pa::fail(PA_ERR_INVALID, "pa_allocate_slots: null pool");
+  if (num_computed < 0 || num_new < 0) return pa::fail(PA_ERR_INVALID, "pa_allocate_slots: negative token count");
+  const int64_t total = num_computed + num_new;
+  const int64_t want = (total + pool->block_size - 1) / pool->block_size;
+  auto it = pool->req_to_blocks.find(req);
+  const int64_t have = it == pool->req_to_blocks.end() ? 0 : int64_t(it->second.size());
+  const int64_t need = want > have ? want - have : 0;
+  if (need > pool->count)
+    return pa::fail(PA_ERR_NO_BLOCKS, "pa_allocate_slots: request %lld needs %lld blocks, %lld free",
+                    (long long)req, (long long)need, (long long)pool->count);
+  if (new_ids_out && need > cap)
+    return pa::fail(PA_ERR_INVALID, "pa_allocate_slots: output capacity %d < %lld new blocks", cap, (long long)need);
+  std::vector<int32_t>& list = pool->req_to_blocks[req];
+  for (int64_t i = 0; i < need; ++i) {
+    int32_t b = pool->pop_front();
+    pool->refcount[b] = 1;
+    list.push_back(b);
+    if (new_ids_out) new_ids_out[i] = b;
+  }
+  if (n_out) *n_out = int32_t(need);
+  return PA_OK;
+}
+
+extern "C" int pa_share_prefix(pa_pool* pool, int64_t req, const int32_t* ids, int32_t n) {
+  pa::clear_error();
+  if (!pool) return pa::fail(PA_ERR_INVALID, "pa_share_prefix: null pool");
+  if (n < 0 || (n > 0 && !ids)) return pa::fail(PA_ERR_INVALID, "pa_share_prefix: bad id list");
+  for (int32_t i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= pool->num_blocks || pool->refcount[ids[i]] <= 0)
+      return pa::fail(PA_ERR_INVALID, "pa_share_prefix: block %d is not allocated", ids[i]);
+  }
+  std::vector<int32_t>& list = pool->req_to_blocks[req];
+  for (int32_t i = 0; i < n; ++i) {
+    pool->refcount[ids[i]] += 1;
+    list.push_back(ids[i]);
+  }
+  return PA_OK;
+}
+
+extern "C" int pa_free(pa_pool* pool, int64_t req) {
+  pa::clear_error();
+  if (!pool) return pa::fail(PA_ERR_INVALID, "pa_free: null pool");
+  auto it = pool->req_to_blocks.find(req);
+  if (it == pool->req_to_blocks.end()) return PA_OK;
+  for (int32_t b : it->second) {
+    if (--pool->refcount[b] == 0) pool->push_back(b);
+  }
+  pool->req_to_blocks.erase(it);
+  return PA_OK;
+}
+
+extern "C" int64_t pa_num_free(const pa_pool* pool) { return pool ? pool->count : -1; }
+
+extern "C" int32_t pa_num_req_blocks(const pa_pool* pool, int64_t req) {
+  if (!pool) return -1;
+  auto it = pool->req_to_blocks.find(req);
+  return it == pool->req_to_blocks.end() ? 0 : int32_t(it->second.size());
+}
+
+extern "C" int32_t pa_refcount(const pa_pool* pool, int32_t block) {
+  if (!pool || block < 0 || block >= pool->num_blocks) return -1;
+  return pool->refcount[block];
+}
+
+extern "C" int pa_block_table_row(const pa_pool* pool, int64_t req, int32_t* out, int32_t width,
+                                  int32_t pad_value) {
+  pa::clear_error();
+  if (!pool || (!out && width > 0) || width < 0) return pa::fail(PA_ERR_INVALID, "pa_block_table_row: bad arguments");
+  auto it = pool->req_to_blocks.find(req);
+  const int64_t n = it == pool->req_to_blocks.end() ? 0 : int64_t(it->second.size());
+  if (n > width)
+    return pa::fail(PA_ERR_INVALID, "pa_block_table_row: request %lld holds %lld blocks > width %d",
+                    (long long)req, (long long)n, width);
+  if (n) std::memcpy(out, it->second.data(), size_t(n) * sizeof(int32_t));
+  for (int64_t i = n; i < width; ++i) out[i] = pad_value;
+  return PA_OK;
+}
+
+extern "C" int pa_slot_mapping(const pa_pool* pool, int64_t req, int64_t start_pos, int32_t n, int32_t* out) {
+  pa::clear_error();
+  if (!pool || n < 0 || (n > 0 && !out) || start_pos < 0) return pa::fail(PA_ERR_INVALID, "pa_slot_mapping: bad arguments");
+  auto it = pool->req_to_blocks.find(req);
+  const int64_t have = it == pool->req_to_blocks.end() ? 0 : int64_t(it->second.size());
+  const int64_t bs = pool->block_size;
+  if (n > 0 && (start_pos + n - 1) / bs >= have)
+    return pa::fail(PA_ERR_INVALID, "pa_slot_mapping: position %lld of request %lld has no block",
+                    (long long)(start_pos + n - 1), (long long)req);
+  for (int32_t j = 0; j < n; ++j) {
+    const int64_t pos = start_pos + j;
+    out[j] = int32_t(int64_t(it->second[pos / bs]) * bs + pos % bs);
+  }
+  return PA_OK;
+}

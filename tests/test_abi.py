@@ -1,0 +1,105 @@
+"""The C-ABI library loads on the host, exports every entry point include/pa.h
+declares, and rejects bad arguments before touching the GPU (CPU only)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_varlen_reshape_amd as pk
+from paged_kv_varlen_reshape_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "pa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    lib = pk.lib()
+    names = header_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_binding_covers_header():
+    assert set(header_functions()) == set(B.SIGNATURES)
+
+
+def _rc(call):
+    return call
+
+
+def test_reshape_rejects_bad_arguments():
+    lib = pk.lib()
+    ok = dict(num_tokens=4, hkv=2, d=64, bs=16, nb=8, dtype=pk.PA_F32)
+
+    def call(num_tokens=4, hkv=2, d=64, bs=16, nb=8, dtype=pk.PA_F32, ptr=1):
+        p = ptr
+        return lib.pa_reshape_and_cache(p, p, p, p, p, num_tokens, hkv, d, bs, nb, dtype, None)
+
+    assert call(d=96) == pk.PA_ERR_UNSUPPORTED
+    assert call(bs=32) == pk.PA_ERR_UNSUPPORTED
+    assert call(dtype=7) == pk.PA_ERR_UNSUPPORTED
+    assert call(hkv=0) == pk.PA_ERR_INVALID
+    assert call(nb=0) == pk.PA_ERR_INVALID
+    assert call(nb=1 << 27) == pk.PA_ERR_INVALID  # slots would not fit in int32
+    assert call(num_tokens=-1) == pk.PA_ERR_INVALID
+    assert call(ptr=None) == pk.PA_ERR_INVALID
+    assert "null" in pk.last_error()
+    assert call(num_tokens=0, ptr=None) == pk.PA_OK  # nothing to do, nothing launched
+    del ok
+
+
+def test_attention_rejects_bad_arguments():
+    lib = pk.lib()
+
+    def call(hq=8, hkv=2, d=128, bs=16, nb=64, mbps=4, S=2, T=3, dtype=pk.PA_BF16, ws=256, ws_bytes=None,
+             ptr=1, scale=0.1):
+        need = lib.pa_attention_workspace_size(S, T, hq, hkv, d, mbps)
+        wsb = need if ws_bytes is None else ws_bytes
+        p = ptr
+        return lib.pa_attention(p, p, p, p, p, p, p, scale, p, S, T, hq, hkv, d, bs, nb, mbps, dtype, ws, wsb, None)
+
+    assert call(hq=6, hkv=4) == pk.PA_ERR_INVALID
+    assert call(hq=32, hkv=2) == pk.PA_ERR_UNSUPPORTED  # group 16 is not built
+    assert call(d=80) == pk.PA_ERR_UNSUPPORTED
+    assert call(bs=8) == pk.PA_ERR_UNSUPPORTED
+    assert call(ws_bytes=16) == pk.PA_ERR_WORKSPACE
+    assert call(ws=0) == pk.PA_ERR_WORKSPACE
+    assert call(ws=257) == pk.PA_ERR_WORKSPACE  # misaligned
+    assert call(ptr=None) == pk.PA_ERR_INVALID
+    assert call(scale=float("nan")) == pk.PA_ERR_INVALID
+    assert call(S=-1) == pk.PA_ERR_INVALID
+    assert call(T=0, ptr=None) == pk.PA_OK
+    assert call(mbps=0) == pk.PA_ERR_INVALID
+
+
+def test_workspace_size_is_deterministic_and_grows():
+    a = pk.pa_attention_workspace_size(64, 64, 32, 8, 128, 129)
+    b = pk.pa_attention_workspace_size(64, 64, 32, 8, 128, 129)
+    c = pk.pa_attention_workspace_size(6148, 8192, 32, 8, 128, 513)
+    assert a == b > 0 and c > a and a % 256 == 0
+    with pytest.raises(pk.PAError):
+        pk.pa_attention_workspace_size(1, 1, 0, 1, 64, 1)
+
+
+def test_options_roundtrip_and_errors():
+    for opt, val in ((pk.PA_OPT_FORCE_ROWWISE, 1), (pk.PA_OPT_SPLIT_TOKENS, 64), (pk.PA_OPT_TARGET_ITEMS, 100)):
+        old = pk.pa_get_option(opt)
+        pk.pa_set_option(opt, val)
+        assert pk.pa_get_option(opt) == val
+        pk.pa_set_option(opt, old)
+    with pytest.raises(pk.PAError):
+        pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, 17)
+    with pytest.raises(pk.PAError):
+        pk.pa_set_option(pk.PA_OPT_FORCE_ROWWISE, 2)
+    with pytest.raises(pk.PAError):
+        pk.pa_set_option(99, 0)

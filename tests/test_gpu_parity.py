@@ -1,0 +1,182 @@
+"""HIP path vs the fp64 oracle on the same seeded inputs (GPU).
+
+Cache scatter: bit-exact, whole pool (poisoned background included).
+Attention: max-abs error <= 1e-5 for float32 steps and <= 1e-2 for bf16 steps
+(inputs bf16, fp32 accumulation), on every row of the small configurations and
+on sampled sequences of the full-size ones, launched exactly as the bench does.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_varlen_reshape_amd as pk
+import workloads as W
+from workloads.device import build_device_step
+from device_data import oracle_rows
+from oracle import ref_reshape_and_cache
+from oracle_data import build_oracle_step
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def _host_bits(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy().view(
+        np.uint16 if t.dtype == torch.bfloat16 else np.uint32)
+
+
+def _check_attention(spec, ds, out, seqs=None):
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all(), "non-finite output (over-read of a poisoned slot?)"
+    seqs = range(spec.num_seqs) if seqs is None else seqs
+    want, got = oracle_rows(spec, seqs, out, ds.meta)
+    err = np.abs(want - got).max() if want.size else 0.0
+    print(f"[{spec.name}] rows={want.shape[0]} max_abs_err={err:.3e}", flush=True)
+    assert err <= TOL[spec.dtype], err
+    return err
+
+
+@pytest.fixture(autouse=True)
+def _reset_options():
+    yield
+    pk.pa_set_option(pk.PA_OPT_FORCE_ROWWISE, 0)
+    pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, 0)
+    pk.pa_set_option(pk.PA_OPT_TARGET_ITEMS, 0)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_reshape_and_cache_bit_exact_whole_pool(cfg):
+    spec = W.make_config(cfg)
+    print(f"reshape parity cfg{cfg}", flush=True)
+    ds = build_device_step(spec, pad_value=-1)
+    ds.reshape()
+    torch.cuda.synchronize()
+    st = build_oracle_step(spec)
+    kc, vc = ref_reshape_and_cache(st.k_new, st.v_new, st.meta.slot_mapping, st.k_cache_pre, st.v_cache_pre, 16)
+    assert np.array_equal(st.meta.block_tables, ds.meta.block_tables)
+    assert np.array_equal(_host_bits(ds.k_cache), kc)
+    assert np.array_equal(_host_bits(ds.v_cache), vc)
+
+
+def test_reshape_skips_negative_slots_and_empty_call():
+    spec = W.random_spec(21, num_seqs=4, dtype="bf16", head_dim=128)
+    ds = build_device_step(spec)
+    before = _host_bits(ds.k_cache).copy()
+    sm = ds.slot_mapping.clone()
+    sm[::2] = -1
+    pk.pa_reshape_and_cache(ds.k_new, ds.v_new, sm, ds.k_cache, ds.v_cache)
+    torch.cuda.synchronize()
+    st = build_oracle_step(spec)
+    kc, _ = ref_reshape_and_cache(st.k_new, st.v_new, sm.cpu().numpy(), before, before, 16)
+    assert np.array_equal(_host_bits(ds.k_cache), kc)
+    pk.pa_reshape_and_cache(ds.k_new[:0], ds.v_new[:0], sm[:0], ds.k_cache, ds.v_cache)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_attention_matches_oracle_every_row(cfg):
+    spec = W.make_config(cfg)
+    print(f"attention parity cfg{cfg}", flush=True)
+    ds = build_device_step(spec)
+    ds.reshape()
+    out = ds.attention()
+    _check_attention(spec, ds, out)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_attention_random_steps(seed):
+    r = np.random.default_rng(seed)
+    dtype = ["f32", "bf16"][seed % 2]
+    hkv = int(r.choice([1, 2, 4]))
+    g = int(r.choice([1, 2, 4, 8]))
+    d = int(r.choice([64, 128]))
+    spec = W.random_spec(seed, num_seqs=int(r.integers(1, 9)), max_context=int(r.integers(1, 300)),
+                         max_query=int(r.integers(1, 40)), num_q_heads=hkv * g, num_kv_heads=hkv, head_dim=d,
+                         dtype=dtype, prefix_tokens=int(r.choice([0, 16, 48])), decode_fraction=0.5)
+    print(f"random step seed={seed} {dtype} hkv={hkv} g={g} d={d} seqs={spec.num_seqs}", flush=True)
+    ds = build_device_step(spec)
+    ds.reshape()
+    for split in (0, 16, 48):
+        pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, split)
+        out = ds.attention()
+        _check_attention(spec, ds, out)
+
+
+def test_forced_rowwise_and_split_sizes_agree():
+    spec = W.make_config(3)
+    ds = build_device_step(spec)
+    ds.reshape()
+    base = ds.attention().clone()
+    pk.pa_set_option(pk.PA_OPT_FORCE_ROWWISE, 1)
+    for split in (16, 256, 4096):
+        pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, split)
+        out = ds.attention()
+        torch.cuda.synchronize()
+        assert (out - base).abs().max().item() <= 2e-2
+
+
+def test_deterministic_bitwise():
+    spec = W.make_config(2)
+    ds = build_device_step(spec)
+    ds.reshape()
+    a = ds.attention().clone()
+    b = ds.attention().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_block_permutation_invariance_on_gpu():
+    spec = W.make_config(2)
+    a = build_device_step(spec)
+    a.reshape()
+    oa = a.attention().clone()
+    spec2 = W.make_config(2)
+    spec2.initial_order = np.random.default_rng(77).permutation(spec2.num_blocks).astype(np.int32)
+    b = build_device_step(spec2)
+    b.reshape()
+    ob = b.attention()
+    torch.cuda.synchronize()
+    assert not np.array_equal(a.meta.block_tables, b.meta.block_tables)
+    assert torch.equal(oa, ob)  # same work decomposition, only addresses differ
+
+
+def test_sequences_without_query_rows_and_padding():
+    spec = W.random_spec(30, num_seqs=6, dtype="bf16", head_dim=128, num_q_heads=8, num_kv_heads=2)
+    spec.requests[1].query = 0
+    spec.requests[4].query = 0
+    ds = build_device_step(spec, pad_value=-1)
+    ds.reshape()
+    out = ds.attention()
+    _check_attention(spec, ds, out)
+
+
+def test_empty_step_is_a_no_op():
+    spec = W.random_spec(31, num_seqs=2, dtype="bf16", head_dim=128, num_q_heads=8, num_kv_heads=2)
+    ds = build_device_step(spec)
+    out = torch.full((0, 8, 128), 0.0, device="cuda")
+    pk.pa_attention(ds.q[:0], ds.k_cache, ds.v_cache, ds.block_tables, ds.seq_lens[:0], ds.query_start_loc[:1],
+                    ds.context_lens[:0], 0.1, out=out)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_full_size_configs_sampled(cfg):
+    spec = W.make_config(cfg)
+    print(f"full-size cfg{cfg}: building {spec.num_blocks} blocks", flush=True)
+    ds = build_device_step(spec)
+    ds.reshape()
+    out = ds.attention()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cfg)
+    if cfg == 4:
+        seqs = list(range(4)) + sorted(rng.choice(np.arange(4, spec.num_seqs), 60, replace=False).tolist())
+    else:
+        seqs = sorted(rng.choice(256, 24, replace=False).tolist()) + [256, 263, 271]
+    _check_attention(spec, ds, out, seqs)
+    # scatter of this step: every written slot holds the step's row, bit for bit
+    sm = ds.meta.slot_mapping.astype(np.int64)
+    blk, off = sm // 16, sm % 16
+    got_k = ds.k_cache[torch.from_numpy(blk).cuda(), :, torch.from_numpy(off).cuda(), :]
+    assert torch.equal(got_k.view(torch.int16), ds.k_new.view(torch.int16))
+    del ds
+    torch.cuda.empty_cache()
