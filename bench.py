@@ -134,10 +134,10 @@ def main(argv=None):
 
     torch.cuda.set_device(0)
     spec = W.make_config(args.config)
-    pool_bytes = 2 * spec.num_blocks * spec.num_kv_heads * 16 * spec.head_dim * spec.elt_bytes
-    reps = args.replicas or max(1, min(8, int((1 << 30) // max(1, pool_bytes)) + 1))
-    if args.config in (4, 5):
-        reps = 1
+    # rotate over enough replicas that the K/V read since a replica's last use
+    # exceeds 1 GiB (4x the 256 MB last-level cache)
+    kv_step = algorithmic_work(spec, False)["kv_unique_bytes"]
+    reps = args.replicas or max(1, min(8, -(-(1 << 30) // max(1, kv_step)) + 1))
     steps = [build_device_step(spec, device="cuda:0") for _ in range(reps)]
     outs = [torch.empty((spec.num_tokens, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device="cuda:0")
             for _ in range(reps)]

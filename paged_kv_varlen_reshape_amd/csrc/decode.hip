@@ -61,14 +61,19 @@ struct DecodeCfg {
   static_assert(LPR == 8 || LPR == 16 || LPR == 32, "unsupported row width");
 };
 
-template <bool BF16, int D, int G>
+// Reinterpret one dword as two bf16.  Taking the dword by value matters: this
+// clang lowers __builtin_bit_cast applied directly to a vector element (v.y)
+// as a read of element 0.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
+
+template <bool BF16>
 __device__ __forceinline__ float chunk_dot(const u32x4& q, const u32x4& k) {
   if constexpr (BF16) {
     float acc = 0.f;
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.x), __builtin_bit_cast(bf16x2_t, k.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.y), __builtin_bit_cast(bf16x2_t, k.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.z), __builtin_bit_cast(bf16x2_t, k.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w), __builtin_bit_cast(bf16x2_t, k.w), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.x), as_bf16x2(k.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.y), as_bf16x2(k.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.z), as_bf16x2(k.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.w), as_bf16x2(k.w), acc, false);
     return acc;
   } else {
     float acc = __uint_as_float(q.x) * __uint_as_float(k.x);
@@ -164,7 +169,7 @@ decode_splitk_kernel(AttnArgs a, Workspace w) {
         const bool valid = tbase + i * RPI < t1;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float d = group_sum<LPR>(chunk_dot<BF16, D, G>(qv[h], kr[i]));
+          const float d = group_sum<LPR>(chunk_dot<BF16>(qv[h], kr[i]));
           s[h][i] = valid ? d * a.scale_log2 : -INFINITY;
         }
       }
