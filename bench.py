@@ -68,6 +68,40 @@ def algorithmic_work(spec, mfma_rows: bool):
                 reshape_bytes=spec.num_tokens * (2 * kv_tok + 4))
 
 
+def measure_ceilings(pk, torch, reps: int = 10):
+    """Measured HBM ceilings on this device: streaming copy of 4 GiB (read + write
+    bytes) and a read-only pass over 8 GiB, each the median of `reps` runs."""
+    dev = "cuda:0"
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(reps):
+            a, b = ev(), ev()
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[len(ts) // 2]
+
+    src = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    dst = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    ms = timed(lambda: pk.pa_measure_copy(dst, src))
+    copy_gbs = 2 * (1 << 32) / (ms * 1e-3) / 1e9
+    del src, dst
+    big = torch.ones(1 << 33, dtype=torch.uint8, device=dev)
+    out = torch.empty(65536, dtype=torch.int32, device=dev)
+    ms = timed(lambda: pk.pa_measure_read(big, out))
+    read_gbs = (1 << 33) / (ms * 1e-3) / 1e9
+    del big, out
+    torch.cuda.empty_cache()
+    return dict(copy_GBps=copy_gbs, read_GBps=read_gbs)
+
+
 def cpu_baseline(spec, seconds: float):
     """The fp64 oracle timed on this host's cores over a bounded sample of the workload."""
     import numpy as np
@@ -119,6 +153,9 @@ def main(argv=None):
     ap.add_argument("--replicas", type=int, default=0, help="input replicas to rotate over (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the copy/read ceiling measurement")
+    ap.add_argument("--opt", action="append", default=[], metavar="NAME=VALUE",
+                    help="library option before the run, e.g. DECODE_BUFFERS=1")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -132,12 +169,16 @@ def main(argv=None):
     import workloads as W
     from workloads.device import build_device_step
 
+    for o in args.opt:
+        name, val = o.split("=")
+        pk.pa_set_option(getattr(pk, "PA_OPT_" + name), int(val))
     torch.cuda.set_device(0)
+    ceil = None if args.no_ceilings else measure_ceilings(pk, torch)
     spec = W.make_config(args.config)
     # rotate over enough replicas that the K/V read since a replica's last use
     # exceeds 1 GiB (4x the 256 MB last-level cache)
     kv_step = algorithmic_work(spec, False)["kv_unique_bytes"]
-    reps = args.replicas or max(1, min(8, -(-(1 << 30) // max(1, kv_step)) + 1))
+    reps = args.replicas or (1 if kv_step >= (1 << 30) else min(8, -(-(1 << 30) // max(1, kv_step)) + 1))
     steps = [build_device_step(spec, device="cuda:0") for _ in range(reps)]
     outs = [torch.empty((spec.num_tokens, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device="cuda:0")
             for _ in range(reps)]
@@ -152,21 +193,25 @@ def main(argv=None):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    pk.pa_profile_enable((1 << pk.PA_K_DECODE) | (1 << pk.PA_K_CHUNK))
-    pk.pa_profile_read()
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    # second pass with HIP-event timing around every kernel launch of the step
+    # (kept out of the step timing above: the extra event records cost time)
+    pk.pa_profile_enable((1 << pk.PA_K_COUNT) - 1)
+    pk.pa_profile_read()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
     prof = pk.pa_profile_read()
     pk.pa_profile_enable(0)
 
     use_mfma = spec.dtype == "bf16" and pk.pa_get_option(pk.PA_OPT_FORCE_ROWWISE) == 0 and prof["chunk_mfma"][0] > 0
     work = algorithmic_work(spec, use_mfma)
     ms = dt * 1e3 / args.steps
-    decode_n, decode_ms = prof["decode_splitk"]
+    decode_n, decode_ms = prof["decode_streamk"]
     chunk_n, chunk_ms = prof["chunk_mfma"]
     decode_avg = decode_ms / decode_n if decode_n else float("nan")
     chunk_avg = chunk_ms / chunk_n if chunk_n else float("nan")
@@ -186,7 +231,10 @@ def main(argv=None):
     else:
         ach = work["decode_kernel_bytes"] / (decode_avg * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS,
-                    traffic=None, kernel="decode_splitk", kernel_avg_us=decode_avg * 1e3)
+                    traffic=None, kernel="decode_streamk", kernel_avg_us=decode_avg * 1e3)
+        if ceil:
+            roof["frac_of_measured_copy"] = ach / ceil["copy_GBps"]
+            roof["frac_of_measured_read"] = ach / ceil["read_GBps"]
     res = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -195,7 +243,8 @@ def main(argv=None):
                    "kv_unique_bytes": work["kv_unique_bytes"], "kv_logical_bytes": work["kv_logical_bytes"],
                    "causal_flops": work["causal_flops"], "replicas": reps},
         "roofline": roof,
-        "kernels_avg_us": {"decode_splitk": decode_avg * 1e3, "chunk_mfma": chunk_avg * 1e3},
+        "kernels_avg_us": {k: (v[1] / v[0] * 1e3 if v[0] else None) for k, v in prof.items()},
+        "ceilings": ceil,
     }
     if not args.no_cpu_baseline:
         cb = cpu_baseline(spec, args.cpu_seconds)

@@ -79,9 +79,10 @@ int pa_reshape_and_cache(const void* k, const void* v, const int32_t* slot_mappi
                          int64_t num_blocks, int32_t dtype, void* stream);
 
 /* Bytes of device workspace pa_attention needs for a step of this shape
- * (work lists, split-K partial results and counters).  Depends only on the
- * arguments, so it can be sized once for the largest step and reused.
- * Returns 0 if the arguments are invalid. */
+ * (work lists, partial results of split rows, counters).  Depends on the
+ * arguments, the current device's compute-unit count and the options, so it
+ * can be sized once for the largest step and reused.  Returns 0 if the
+ * arguments are invalid. */
 size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t head_dim,
                                    int32_t max_blocks_per_seq);
@@ -133,9 +134,14 @@ const char* pa_last_error(void);
 
 /* Tuning and debug options (process-wide).  Returns PA_OK or PA_ERR_INVALID. */
 enum {
-  PA_OPT_FORCE_ROWWISE = 1, /* 1: every query row takes the row-wise VALU kernel, MFMA off */
-  PA_OPT_SPLIT_TOKENS = 2,  /* >0: fixed split-K partition in tokens (multiple of 16); 0: automatic */
-  PA_OPT_TARGET_ITEMS = 3   /* >0: work items the automatic split aims at; 0: default */
+  PA_OPT_FORCE_ROWWISE = 1,  /* 1: every query row takes the row-wise VALU kernel, MFMA off */
+  PA_OPT_SPLIT_TOKENS = 2,   /* >0: each decode wavefront range covers this many tokens' worth of
+                                (row, kv head) pages (multiple of 16); 0: automatic, the step's
+                                pages spread evenly over the resident wavefronts */
+  PA_OPT_TARGET_ITEMS = 3,   /* >0: number of decode ranges in automatic mode; 0: one per
+                                resident decode wavefront */
+  PA_OPT_DECODE_BUFFERS = 4  /* 1 or 2: pages in registers per decode wavefront (2 = the next
+                                page's loads overlap this page's math); 0: automatic */
 };
 int pa_set_option(int32_t option, int64_t value);
 int64_t pa_get_option(int32_t option);
@@ -148,7 +154,7 @@ int64_t pa_get_option(int32_t option);
  * and their summed duration in milliseconds into counts / total_ms (host
  * arrays of PA_K_COUNT entries, either may be NULL) and clears the record.
  * mask 0 (the default) records nothing. */
-enum { PA_K_RESHAPE = 0, PA_K_PLAN = 1, PA_K_CHUNK = 2, PA_K_DECODE = 3, PA_K_REDUCE = 4, PA_K_COUNT = 5 };
+enum { PA_K_RESHAPE = 0, PA_K_PLAN = 1, PA_K_CHUNK = 2, PA_K_DECODE = 3, PA_K_MERGE = 4, PA_K_COUNT = 5 };
 int pa_profile_enable(int32_t mask);
 int pa_profile_read(int64_t* counts, double* total_ms);
 

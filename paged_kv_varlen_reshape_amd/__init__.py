@@ -19,10 +19,12 @@ from ._binding import (  # noqa: F401
     PA_OPT_FORCE_ROWWISE,
     PA_OPT_SPLIT_TOKENS,
     PA_OPT_TARGET_ITEMS,
+    PA_OPT_DECODE_BUFFERS,
     PA_K_CHUNK,
+    PA_K_COUNT,
     PA_K_DECODE,
+    PA_K_MERGE,
     PA_K_PLAN,
-    PA_K_REDUCE,
     PA_K_RESHAPE,
     KERNEL_NAMES,
     SIGNATURES,
@@ -31,6 +33,8 @@ from ._binding import (  # noqa: F401
     pa_attention,
     pa_attention_workspace_size,
     pa_get_option,
+    pa_measure_copy,
+    pa_measure_read,
     pa_profile_enable,
     pa_profile_read,
     pa_reshape_and_cache,

@@ -27,8 +27,9 @@ PA_BF16 = 1
 PA_OPT_FORCE_ROWWISE = 1
 PA_OPT_SPLIT_TOKENS = 2
 PA_OPT_TARGET_ITEMS = 3
-PA_K_RESHAPE, PA_K_PLAN, PA_K_CHUNK, PA_K_DECODE, PA_K_REDUCE, PA_K_COUNT = range(6)
-KERNEL_NAMES = ["reshape_and_cache", "plan", "chunk_mfma", "decode_splitk", "splitk_reduce"]
+PA_OPT_DECODE_BUFFERS = 4
+PA_K_RESHAPE, PA_K_PLAN, PA_K_CHUNK, PA_K_DECODE, PA_K_MERGE, PA_K_COUNT = range(6)
+KERNEL_NAMES = ["reshape_and_cache", "plan", "chunk_mfma", "decode_streamk", "split_merge"]
 
 _i32, _i64, _f32, _vp, _sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
 _pi32 = C.POINTER(C.c_int32)
@@ -45,6 +46,8 @@ SIGNATURES = {
     "pa_get_option": (_i64, [_i32]),
     "pa_profile_enable": (_i32, [_i32]),
     "pa_profile_read": (_i32, [C.POINTER(C.c_int64), C.POINTER(C.c_double)]),
+    "pa_measure_copy": (_i32, [_vp, _vp, _sz, _vp]),
+    "pa_measure_read": (_i32, [_vp, _sz, _vp, _vp]),
     "pa_pool_create": (_vp, [_i64, _i32, _pi32]),
     "pa_pool_destroy": (None, [_vp]),
     "pa_allocate_slots": (_i32, [_vp, _i64, _i64, _i64, _pi32, _i32, _pi32]),
@@ -174,6 +177,22 @@ def pa_attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, c
                               _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                               _stream_handle(q.device)))
     return out
+
+
+def pa_measure_copy(dst, src) -> None:
+    """Streaming copy of src into dst (device tensors of the same byte size)."""
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("size mismatch")
+    _check(lib().pa_measure_copy(_dev_ptr(dst, "dst"), _dev_ptr(src, "src"), nb, _stream_handle(src.device)))
+
+
+def pa_measure_read(src, out) -> None:
+    """Read-only pass over src; out is an int32 device tensor of >= 65536 entries."""
+    if out.numel() < 65536 or out.dtype.itemsize != 4:
+        raise ValueError("out must hold 65536 32-bit entries")
+    _check(lib().pa_measure_read(_dev_ptr(src, "src"), src.numel() * src.element_size(), _dev_ptr(out, "out"),
+                                 _stream_handle(src.device)))
 
 
 # ----------------------------------------------------------------- host calls

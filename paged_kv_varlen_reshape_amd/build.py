@@ -29,7 +29,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 SOURCES = ["errors.cpp", "pool.cpp", "validate.cpp", "api.hip", "reshape.hip", "plan.hip",
-           "decode.hip", "chunk.hip"]
+           "decode.hip", "chunk.hip", "measure.hip"]
 
 
 def _compile(src: str, opt: list[str]) -> str:

@@ -1,5 +1,5 @@
 // C-ABI entry points of libpa: argument checks, workspace layout and the
-// launch sequence of one step (scatter; plan -> chunk -> row-wise -> reduce).
+// launch sequence of one step (scatter; plan -> chunk -> row-wise split-K -> split merge).
 #include <atomic>
 #include <cmath>
 #include <mutex>
@@ -69,11 +69,6 @@ namespace {
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-int64_t target_items() {
-  const int64_t t = option(PA_OPT_TARGET_ITEMS);
-  return t > 0 ? t : kDefaultTargetItems;
-}
-
 int check_dims(int32_t hkv, int32_t d, int32_t bs, int32_t dtype, int64_t nb, const char* who) {
   if (hkv <= 0) return fail(PA_ERR_INVALID, "%s: num_kv_heads must be positive", who);
   if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d not supported", who, dtype);
@@ -86,19 +81,27 @@ int check_dims(int32_t hkv, int32_t d, int32_t bs, int32_t dtype, int64_t nb, co
 
 }  // namespace
 
+int64_t ranges_capacity(const StepShape& s) {
+  int64_t cap = int64_t(device_cus()) * kMaxWavesPerCU;
+  const int64_t want = option(PA_OPT_TARGET_ITEMS);
+  if (want > cap) cap = want;
+  const int64_t fixed = option(PA_OPT_SPLIT_TOKENS) / kBlock;
+  if (fixed > 0) {
+    const int64_t units = int64_t(s.num_tokens) * s.num_kv_heads * s.max_blocks_per_seq;
+    int64_t n = (units + fixed - 1) / fixed;
+    if (n > (int64_t(1) << 20)) n = int64_t(1) << 20;  // the plan lengthens ranges beyond this
+    if (n > cap) cap = n;
+  }
+  return cap;
+}
+
 Workspace layout_workspace(const StepShape& s, void* ws) {
   Workspace w{};
   const int64_t T = s.num_tokens > 0 ? s.num_tokens : 1;
+  const int64_t G = s.num_kv_heads > 0 ? s.num_q_heads / s.num_kv_heads : 1;
   w.rows_cap = T;
   w.tiles_cap = T;
-  const int64_t fixed = option(PA_OPT_SPLIT_TOKENS);
-  if (fixed > 0) {
-    const int64_t max_keys = int64_t(s.max_blocks_per_seq) * kBlock;
-    w.splits_cap = w.rows_cap * ((max_keys + fixed - 1) / fixed);
-  } else {
-    w.splits_cap = (target_items() + s.num_kv_heads - 1) / s.num_kv_heads + w.rows_cap;
-  }
-  if (w.splits_cap < 1) w.splits_cap = 1;
+  w.ranges_cap = ranges_capacity(s);
   char* p = static_cast<char*>(ws);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -107,15 +110,14 @@ Workspace layout_workspace(const StepShape& s, void* ws) {
     return r;
   };
   w.hdr = reinterpret_cast<int32_t*>(take(H_WORDS * sizeof(int32_t)));
-  w.row_tok = reinterpret_cast<int32_t*>(take(w.rows_cap * sizeof(int32_t)));
-  w.row_seq = reinterpret_cast<int32_t*>(take(w.rows_cap * sizeof(int32_t)));
-  w.row_len = reinterpret_cast<int32_t*>(take(w.rows_cap * sizeof(int32_t)));
-  w.split_base = reinterpret_cast<int32_t*>(take((w.rows_cap + 1) * sizeof(int32_t)));
-  w.items = reinterpret_cast<int4*>(take(w.splits_cap * sizeof(int4)));
-  w.reduce = reinterpret_cast<int4*>(take(w.rows_cap * sizeof(int4)));
+  w.hdr64 = reinterpret_cast<int64_t*>(w.hdr ? w.hdr + H64 : nullptr);
+  w.rows = reinterpret_cast<int4*>(take(w.rows_cap * sizeof(int4)));
+  w.rows_base = reinterpret_cast<int64_t*>(take(w.rows_cap * sizeof(int64_t)));
   w.tiles = reinterpret_cast<int2*>(take(w.tiles_cap * sizeof(int2)));
-  w.part_o = reinterpret_cast<float*>(take(size_t(w.splits_cap) * s.num_q_heads * s.head_dim * sizeof(float)));
-  w.part_ml = reinterpret_cast<float2*>(take(size_t(w.splits_cap) * s.num_q_heads * sizeof(float2)));
+  w.range_row = reinterpret_cast<int32_t*>(take(w.ranges_cap * sizeof(int32_t)));
+  w.range_cut = reinterpret_cast<int2*>(take(w.ranges_cap * sizeof(int2)));
+  w.part_o = reinterpret_cast<float*>(take(size_t(2 * w.ranges_cap * G) * s.head_dim * sizeof(float)));
+  w.part_ml = reinterpret_cast<float2*>(take(size_t(2 * w.ranges_cap * G) * sizeof(float2)));
   w.bytes = off;
   return w;
 }
@@ -134,6 +136,8 @@ extern "C" int pa_reshape_and_cache(const void* k, const void* v, const int32_t*
   if (!k || !v || !slot_mapping || !k_cache || !v_cache)
     return fail(PA_ERR_INVALID, "pa_reshape_and_cache: null pointer");
   const int32_t row_bytes = head_dim * (dtype == PA_BF16 ? 2 : 4);
+  if (int64_t(num_tokens) * num_kv_heads * (row_bytes / 16) >= (int64_t(1) << 31))
+    return fail(PA_ERR_INVALID, "pa_reshape_and_cache: num_tokens * num_kv_heads too large for one call");
   hipError_t e;
   {
     KernelTimer t(PA_K_RESHAPE, static_cast<hipStream_t>(stream));
@@ -196,8 +200,14 @@ extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_ca
   pa_args.num_kv_heads = num_kv_heads;
   pa_args.max_len = max_blocks_per_seq * kBlock;
   pa_args.use_mfma = use_mfma ? 1 : 0;
-  pa_args.fixed_split = int32_t(option(PA_OPT_SPLIT_TOKENS));
-  pa_args.target_items = int32_t(target_items());
+  pa_args.fixed_units = int32_t(option(PA_OPT_SPLIT_TOKENS) / kBlock);
+  {
+    const int64_t want = option(PA_OPT_TARGET_ITEMS);
+    int64_t n = want > 0 ? want : decode_waves(bf16 ? 1 : 0, head_dim, group);
+    if (n > w.ranges_cap) n = w.ranges_cap;
+    pa_args.num_ranges = int32_t(n < 1 ? 1 : n);
+  }
+  pa_args.tile_rows = use_mfma ? chunk_tile_rows(group) : 1;
 
   AttnArgs a{};
   a.q = q;
@@ -232,8 +242,8 @@ extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_ca
     e = launch_decode(a, w, group, st);
   }
   if (e == hipSuccess) {
-    KernelTimer t(PA_K_REDUCE, st);
-    e = launch_reduce(a, w, group, st);
+    KernelTimer t(PA_K_MERGE, st);
+    e = launch_merge(a, w, group, st);
   }
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_attention: launch failed: %s", hipGetErrorString(e));
   return PA_OK;

@@ -4,5 +4,6 @@
 
 namespace pa {
 bool chunk_supported(int, int, int) { return false; }
+int chunk_tile_rows(int) { return 32; }
 hipError_t launch_chunk(const AttnArgs&, const Workspace&, int, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace pa

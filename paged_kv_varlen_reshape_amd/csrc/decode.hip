@@ -1,27 +1,35 @@
-// decode_splitk + splitk_reduce: row-wise attention over the paged cache on the VALU.
+// decode_streamk + split_merge: row-wise attention over the paged cache on the VALU.
 //
 // Decoding reads the whole cached context of a request for one new token, so
 // it is bound by memory bandwidth (Inside vLLM summary, techfeed.io, section
 // "エンジンの中核：スケジューラとKVキャッシュ管理"); the cache is held in
 // 16-token blocks reached through each request's block list (same page,
-// section "PagedAttentionの仕組み").  Each work item is one (query row, kv
-// head, split of P tokens); a row at absolute position p sees keys 0..p.  The
-// same kernel serves decodes, float32 steps and every row of a chunk when the
-// MFMA path is off.
+// section "PagedAttentionの仕組み").  A row at absolute position p sees keys
+// 0..p.  The same kernel serves decodes, float32 steps and every row of a
+// chunk when the MFMA path is off.
 //
-// Work item -> workgroup of 4 wavefronts.  Wave w takes pages w, w+4, ... of
-// the split.  A page of one kv head is one contiguous 16*D*elt run; a wave
-// reads it with 16-byte lanes, so each load instruction is a fully coalesced
-// 1 KiB: lane = (token row within the instruction, 16-byte chunk of the row).
-// The GQA group's G query heads share every K/V load.  Scores: dot products of
-// the lane's chunk (bf16 pairs on v_dot2_f32_bf16, float32 by FMA), summed
-// across the lanes of a token row with DPP.  Online softmax per lane row in the
-// log2 domain; at the end the rows of a wave merge by shuffles and the four
-// waves by LDS, and the item writes either the normalised output (one split)
-// or its unnormalised partial (o, max, sum) for splitk_reduce.
+// Work decomposition (stream-K).  The plan lays every (row, kv head, page)
+// unit of the step in one stream and cuts it into equal ranges, one per
+// resident wavefront, so every wavefront streams the same number of pages:
+// no atomics, no barriers, no tail of uneven items.  A range walks one or more
+// segments (a run of pages of one (row, kv head)); a segment that covers its
+// whole (row, kv head) writes the normalised output, one that a range
+// boundary cuts writes its unnormalised partial (o, max, sum) and split_merge
+// folds the pieces.
 //
-// Algorithmic HBM traffic per item: 2 * split_tokens * D * elt of K/V, plus
-// G * D * elt of q and G * D * 4 of output or partial.
+// Inside a segment the wavefront keeps the block ids of up to 64 pages in one
+// register (lane j holds page j) and issues each page's K/V loads while the
+// previous page is scored (two register buffers).  A page of one kv head is
+// one contiguous 16*D*elt run read with 16-byte lanes, so each load
+// instruction is a fully coalesced 1 KiB: lane = (token row within the
+// instruction, 16-byte chunk of the row).  The GQA group's G query heads share
+// every K/V load.  Scores: dot products of the lane's chunk (bf16 pairs on
+// v_dot2_f32_bf16, float32 by FMA), summed across the lanes of a token row with
+// DPP.  Online softmax per lane row in the log2 domain; at the end of a segment
+// the lane rows merge by shuffles.
+//
+// Algorithmic HBM traffic per unit: 2 * 16 * D * elt bytes of K/V; per
+// segment G * D * elt of q and G * D * 4 of output or partial.
 #include "internal.h"
 
 namespace pa {
@@ -57,7 +65,6 @@ struct DecodeCfg {
   static constexpr int LPR = D / VEC;      // lanes per token row
   static constexpr int RPI = kWave / LPR;  // token rows per load instruction
   static constexpr int IPP = kBlock / RPI; // load instructions per 16-token page
-  static constexpr int NW = kDecodeThreads / kWave;
   static_assert(LPR == 8 || LPR == 16 || LPR == 32, "unsupported row width");
 };
 
@@ -95,251 +102,371 @@ __device__ __forceinline__ void unpack(const u32x4& v, float* e) {
   }
 }
 
-template <bool BF16, int D, int G>
-__global__ void __launch_bounds__(kDecodeThreads)
-decode_splitk_kernel(AttnArgs a, Workspace w) {
-  using C = DecodeCfg<BF16, D, G>;
-  constexpr int VEC = C::VEC, LPR = C::LPR, RPI = C::RPI, IPP = C::IPP, NW = C::NW;
-  constexpr int ROW_BYTES = D * C::ELT;
+// One 16-token page of one kv head: IPP 16-byte chunks per lane for K and for V.
+template <int IPP>
+struct PageRegs {
+  u32x4 k[IPP], v[IPP];
+};
 
-  __shared__ float s_o[NW][G][D];
-  __shared__ float s_m[NW][G];
-  __shared__ float s_l[NW][G];
-  __shared__ int s_next;
+template <int IPP>
+__device__ __forceinline__ void load_page(PageRegs<IPP>& r, const char* kbase, const char* vbase, int64_t off,
+                                          int lane) {
+  const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + off);
+  const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + off);
+#pragma unroll
+  for (int i = 0; i < IPP; ++i) r.k[i] = __builtin_nontemporal_load(kp + i * kWave + lane);
+#pragma unroll
+  for (int i = 0; i < IPP; ++i) r.v[i] = __builtin_nontemporal_load(vp + i * kWave + lane);
+}
+
+// Scores of one page for the G heads and the online-softmax update of (m, l, o).
+// tbase: position of this lane's first token row; t1: first position not seen.
+template <bool BF16, int D, int G>
+__device__ __forceinline__ void page_update(PageRegs<DecodeCfg<BF16, D, G>::IPP>& r, const u32x4 (&qv)[G],
+                                            int tbase, int t1, bool partial, float scale_log2, float (&m)[G],
+                                            float (&l)[G], float (&o)[G][DecodeCfg<BF16, D, G>::VEC]) {
+  using C = DecodeCfg<BF16, D, G>;
+  constexpr int VEC = C::VEC, LPR = C::LPR, RPI = C::RPI, IPP = C::IPP;
+  float s[G][IPP];
+#pragma unroll
+  for (int i = 0; i < IPP; ++i) {
+    const bool valid = tbase + i * RPI < t1;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float d = group_sum<LPR>(chunk_dot<BF16>(qv[h], r.k[i]));
+      s[h][i] = valid ? d * scale_log2 : -INFINITY;
+    }
+  }
+  if (partial) {  // last, partly filled page: masked rows must not reach PV (NaN-safe)
+#pragma unroll
+    for (int i = 0; i < IPP; ++i)
+      if (tbase + i * RPI >= t1) r.v[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // rescale the running sums to the new maxima; scores become weights in place
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mx = s[h][0];
+#pragma unroll
+    for (int i = 1; i < IPP; ++i) mx = fmaxf(mx, s[h][i]);
+    const float m_new = fmaxf(m[h], mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m[h] - m_use);
+    float lsum = l[h] * alpha;
+#pragma unroll
+    for (int i = 0; i < IPP; ++i) {
+      s[h][i] = fast_exp2(s[h][i] - m_use);
+      lsum += s[h][i];
+    }
+    l[h] = lsum;
+    m[h] = m_new;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[h][e] *= alpha;
+  }
+  // PV, token-outer: one token row's V elements are live at a time
+#pragma unroll
+  for (int i = 0; i < IPP; ++i) {
+    float ve[VEC];
+    unpack<BF16>(r.v[i], ve);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[h][e] = fmaf(s[h][i], ve[e], o[h][e]);
+  }
+}
+
+template <bool BF16, int D, int G, int NBUF>
+__global__ void __launch_bounds__(256)
+decode_streamk_kernel(AttnArgs a, Workspace w) {
+  using C = DecodeCfg<BF16, D, G>;
+  constexpr int VEC = C::VEC, LPR = C::LPR, IPP = C::IPP;
+  constexpr int ROW_BYTES = D * C::ELT;
+  constexpr int WPB = 256 / kWave;  // wavefronts per workgroup
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
   const int lr = lane / LPR;  // token row of this lane within a load instruction
   const int lc = lane % LPR;  // 16-byte chunk of the row
+  const int gwave = blockIdx.x * WPB + threadIdx.x / kWave;
+  const int nwaves = gridDim.x * WPB;
 
-  const int64_t n_items = int64_t(w.hdr[H_SPLITS]) * a.hkv;
-  const int P = w.hdr[H_SPLIT_TOKENS];
+  const int nranges = w.hdr[H_RANGES];
+  const int64_t units = w.hdr64[H64_UNITS];
+  const int64_t per = w.hdr64[H64_PER];
   const int64_t page_stride = int64_t(kBlock) * ROW_BYTES;  // bytes of one (block, kv head) page
   const char* kbase = static_cast<const char*>(a.kc);
   const char* vbase = static_cast<const char*>(a.vc);
 
-  for (int64_t item = blockIdx.x; item < n_items;) {
-    if (threadIdx.x == 0) s_next = int(gridDim.x) + atomicAdd(&w.hdr[H_COUNTER], 1);
+  for (int g = gwave; g < nranges; g += nwaves) {
+    int64_t x = g * per;
+    const int64_t x_end = min(x + per, units);
+    int r = w.range_row[g];
+    int4 rec = w.rows[r];
+    int64_t base = w.rows_base[r];
+    int pages = (rec.z + kBlock - 1) / kBlock;
+    int kvh = int((x - base) / pages);
+    int p0 = int(x - base - int64_t(kvh) * pages);
+    bool first = true;
 
-    const int64_t u = item / a.hkv;
-    const int kvh = int(item - u * a.hkv);
-    const int4 rec = w.items[u];
-    const int tok = rec.x, seq = rec.y, len = rec.z;
-    const int split = rec.w & (kSingleSplit - 1);
-    const bool single = (rec.w & kSingleSplit) != 0;
-    const int t0 = split * P;
-    const int t1 = min(t0 + P, len);
-    const int pg0 = t0 / kBlock, pg1 = (t1 + kBlock - 1) / kBlock;
-    const int32_t* btrow = a.bt + int64_t(seq) * a.mbps;
+    while (x < x_end) {
+      const int tok = rec.x, seq = rec.y, len = rec.z;
+      const int n = int(min(int64_t(pages - p0), x_end - x));  // pages of this segment
+      const int32_t* btrow = a.bt + int64_t(seq) * a.mbps + p0;
 
-    // query chunks of the G heads of this kv head
-    u32x4 qv[G];
-    {
-      const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) +
-                                                       (int64_t(tok) * a.hq + int64_t(kvh) * G) * ROW_BYTES);
+      // query chunks of the G heads of this kv head
+      u32x4 qv[G];
+      {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) +
+                                                         (int64_t(tok) * a.hq + int64_t(kvh) * G) * ROW_BYTES);
 #pragma unroll
-      for (int h = 0; h < G; ++h) qv[h] = qp[h * LPR + lc];
-    }
-
-    float m[G], l[G], o[G][VEC];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      m[h] = -INFINITY;
-      l[h] = 0.f;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) o[h][e] = 0.f;
-    }
-
-    for (int pg = pg0 + wave; pg < pg1; pg += NW) {
-      int64_t blk = btrow[pg];
-      blk = blk < 0 ? 0 : (blk >= a.nb ? a.nb - 1 : blk);  // never leave the pool
-      const int64_t poff = (blk * a.hkv + kvh) * page_stride;
-      const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + poff);
-      const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + poff);
-      u32x4 kr[IPP], vr[IPP];
-#pragma unroll
-      for (int i = 0; i < IPP; ++i) kr[i] = __builtin_nontemporal_load(kp + i * kWave + lane);
-#pragma unroll
-      for (int i = 0; i < IPP; ++i) vr[i] = __builtin_nontemporal_load(vp + i * kWave + lane);
-
-      const int tbase = pg * kBlock + lr;
-      float s[G][IPP];
-#pragma unroll
-      for (int i = 0; i < IPP; ++i) {
-        const bool valid = tbase + i * RPI < t1;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float d = group_sum<LPR>(chunk_dot<BF16>(qv[h], kr[i]));
-          s[h][i] = valid ? d * a.scale_log2 : -INFINITY;
-        }
+        for (int h = 0; h < G; ++h) qv[h] = qp[h * LPR + lc];
       }
-      if (pg * kBlock + kBlock > t1) {  // last, partly filled page: masked rows must not reach PV
-#pragma unroll
-        for (int i = 0; i < IPP; ++i)
-          if (tbase + i * RPI >= t1) vr[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-      float ve[IPP][VEC];
-#pragma unroll
-      for (int i = 0; i < IPP; ++i) unpack<BF16>(vr[i], ve[i]);
 
+      float m[G], l[G], o[G][VEC];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float mx = s[h][0];
+        m[h] = -INFINITY;
+        l[h] = 0.f;
 #pragma unroll
-        for (int i = 1; i < IPP; ++i) mx = fmaxf(mx, s[h][i]);
-        const float m_new = fmaxf(m[h], mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m[h] - m_use);
-        float lsum = l[h] * alpha;
-        float acc[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = o[h][e] * alpha;
-#pragma unroll
-        for (int i = 0; i < IPP; ++i) {
-          const float p = fast_exp2(s[h][i] - m_use);
-          lsum += p;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[e] = fmaf(p, ve[i][e], acc[e]);
-        }
-        l[h] = lsum;
-        m[h] = m_new;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) o[h][e] = acc[e];
+        for (int e = 0; e < VEC; ++e) o[h][e] = 0.f;
       }
-    }
 
-    // merge the RPI lane rows of this wave (lanes that differ above the row width)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float M = m[h];
-#pragma unroll
-      for (int x = LPR; x < kWave; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
-      const float f = m[h] == -INFINITY ? 0.f : fast_exp2(m[h] - M);
-      float lsum = l[h] * f;
-#pragma unroll
-      for (int x = LPR; x < kWave; x <<= 1) lsum += __shfl_xor(lsum, x);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        float v = o[h][e] * f;
-#pragma unroll
-        for (int x = LPR; x < kWave; x <<= 1) v += __shfl_xor(v, x);
-        o[h][e] = v;
-      }
-      if (lr == 0) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) s_o[wave][h][lc * VEC + e] = o[h][e];
-        if (lc == 0) {
-          s_m[wave][h] = M;
-          s_l[wave][h] = lsum;
-        }
-      }
-    }
-    __syncthreads();
+      // block ids of the segment's pages, 64 at a time: lane j holds page j of the batch
+      int32_t ids = 0;
+      auto load_ids = [&](int j0) {
+        const int j = j0 + lane;
+        const int32_t b = j < n ? btrow[j] : 0;
+        ids = b < 0 ? 0 : (b >= a.nb ? int32_t(a.nb - 1) : b);  // never leave the pool
+      };
+      auto page_off = [&](int j) -> int64_t {
+        const int32_t b = __builtin_amdgcn_readlane(ids, j & (kWave - 1));
+        return (int64_t(b) * a.hkv + kvh) * page_stride;
+      };
+      auto pos = [&](int j) { return (p0 + j) * kBlock; };
 
-    // merge the waves and write
-    for (int e = threadIdx.x; e < G * D; e += kDecodeThreads) {
-      const int h = e / D, d = e - h * D;
-      float M = s_m[0][h];
-#pragma unroll
-      for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, s_m[ww][h]);
-      float acc = 0.f, lsum = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float mw = s_m[ww][h];
-        const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-        acc = fmaf(f, s_o[ww][h][d], acc);
-        lsum = fmaf(f, s_l[ww][h], lsum);
-      }
-      const int64_t head = int64_t(kvh) * G + h;
-      if (single) {
-        a.out[(int64_t(tok) * a.hq + head) * D + d] = acc / lsum;
+      load_ids(0);
+      if constexpr (NBUF == 2) {
+        PageRegs<IPP> ra, rb;
+        load_page<IPP>(ra, kbase, vbase, page_off(0), lane);
+        for (int j = 0; j < n; j += 2) {
+          // the next page's loads are in flight while this one is scored
+          if (j + 1 < n) {
+            if (((j + 1) & (kWave - 1)) == 0) load_ids(j + 1);
+            load_page<IPP>(rb, kbase, vbase, page_off(j + 1), lane);
+          }
+          page_update<BF16, D, G>(ra, qv, pos(j) + lr, len, pos(j) + kBlock > len, a.scale_log2, m, l, o);
+          if (j + 1 >= n) break;
+          if (j + 2 < n) {
+            if (((j + 2) & (kWave - 1)) == 0) load_ids(j + 2);
+            load_page<IPP>(ra, kbase, vbase, page_off(j + 2), lane);
+          }
+          page_update<BF16, D, G>(rb, qv, pos(j + 1) + lr, len, pos(j + 1) + kBlock > len, a.scale_log2, m, l, o);
+        }
       } else {
-        const int64_t pi = u * a.hq + head;
-        w.part_o[pi * D + d] = acc;
-        if (d == 0) w.part_ml[pi] = make_float2(M, lsum);
+        for (int j = 0; j < n; ++j) {
+          if (j > 0 && (j & (kWave - 1)) == 0) load_ids(j);
+          PageRegs<IPP> ra;
+          load_page<IPP>(ra, kbase, vbase, page_off(j), lane);
+          page_update<BF16, D, G>(ra, qv, pos(j) + lr, len, pos(j) + kBlock > len, a.scale_log2, m, l, o);
+        }
+      }
+
+      // merge the RPI lane rows (lanes that differ above the row width), then
+      // the lanes of token row 0 hold the segment's result
+      const bool whole = p0 == 0 && n == pages;
+      const int64_t slot = int64_t(g) * 2 + (first ? 0 : 1);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float M = m[h];
+#pragma unroll
+        for (int xx = LPR; xx < kWave; xx <<= 1) M = fmaxf(M, __shfl_xor(M, xx));
+        const float f = m[h] == -INFINITY ? 0.f : fast_exp2(m[h] - M);
+        float lsum = l[h] * f;
+#pragma unroll
+        for (int xx = LPR; xx < kWave; xx <<= 1) lsum += __shfl_xor(lsum, xx);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          float v = o[h][e] * f;
+#pragma unroll
+          for (int xx = LPR; xx < kWave; xx <<= 1) v += __shfl_xor(v, xx);
+          o[h][e] = v;
+        }
+        if (lr == 0) {
+          if (whole) {
+            const float inv = 1.f / lsum;
+            float* op = a.out + (int64_t(tok) * a.hq + int64_t(kvh) * G + h) * D + lc * VEC;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) op[e] = o[h][e] * inv;
+          } else {
+            float* po = w.part_o + (slot * G + h) * D + lc * VEC;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) po[e] = o[h][e];
+            if (lc == 0) w.part_ml[slot * G + h] = make_float2(M, lsum);
+          }
+        }
+      }
+
+      x += n;
+      first = false;
+      if (x < x_end) {  // next (row, kv head)
+        p0 = 0;
+        if (++kvh == a.hkv) {
+          kvh = 0;
+          rec = w.rows[++r];
+          base = w.rows_base[r];
+          pages = (rec.z + kBlock - 1) / kBlock;
+        }
       }
     }
-    __syncthreads();
-    item = s_next;
-    __syncthreads();
   }
 }
 
-// Merge the splits of rows that were cut into more than one:
+// split_merge: (row, kv head) pairs cut by range boundaries.  Range g's start
+// first cuts the pair (r, k) recorded for it; the pair's pieces are the last
+// segment of the range holding its first unit (slot 0 if that range starts
+// exactly there, else slot 1) and the first segment (slot 0) of every later
+// range up to the one holding its last unit.  One wavefront per (cut, query
+// head of the group) folds the pieces with a running maximum:
 //   M = max_s m_s;  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
-template <int D>
+// Each lane owns D/64 consecutive elements, so every piece is one coalesced
+// load per wavefront.
+template <int D, int G>
 __global__ void __launch_bounds__(256)
-splitk_reduce_kernel(AttnArgs a, Workspace w) {
-  const int64_t n = int64_t(w.hdr[H_REDUCE]) * a.hkv;
-  const int G = a.hq / a.hkv;
-  for (int64_t job = blockIdx.x; job < n; job += gridDim.x) {
-    const int64_t r = job / a.hkv;
-    const int kvh = int(job - r * a.hkv);
-    const int4 rec = w.reduce[r];
-    const int tok = rec.x, u0 = rec.y, ns = rec.z;
-    for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-      const int h = e / D, d = e - h * D;
-      const int64_t head = int64_t(kvh) * G + h;
-      float M = -INFINITY;
-      for (int s = 0; s < ns; ++s) M = fmaxf(M, w.part_ml[(int64_t(u0) + s) * a.hq + head].x);
-      float acc = 0.f, lsum = 0.f;
-      for (int s = 0; s < ns; ++s) {
-        const int64_t pi = (int64_t(u0) + s) * a.hq + head;
-        const float2 ml = w.part_ml[pi];
-        const float f = ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - M);
-        acc = fmaf(f, w.part_o[pi * D + d], acc);
-        lsum = fmaf(f, ml.y, lsum);
-      }
-      a.out[(int64_t(tok) * a.hq + head) * D + d] = acc / lsum;
+split_merge_kernel(AttnArgs a, Workspace w) {
+  constexpr int E = D / kWave;  // elements per lane: 1 or 2
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t n_jobs = int64_t(w.hdr[H_RANGES]) * G;
+  const int64_t per = w.hdr64[H64_PER];
+  const int64_t waves = int64_t(gridDim.x) * (blockDim.x / kWave);
+  for (int64_t job = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave; job < n_jobs; job += waves) {
+    const int64_t g = job / G;
+    const int h = int(job - g * G);
+    const int2 cut = w.range_cut[g];
+    if (g == 0 || cut.x < 0) continue;
+    const int4 rec = w.rows[cut.x];
+    const int64_t pages = (rec.z + kBlock - 1) / kBlock;
+    const int64_t f = w.rows_base[cut.x] + cut.y * pages;  // first unit of the pair
+    const int64_t g0 = f / per, g1 = (f + pages - 1) / per;
+    float M = -INFINITY, lsum = 0.f, acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int64_t gg = g0; gg <= g1; ++gg) {
+      const int64_t slot = gg * 2 + (gg == g0 && f != g0 * per ? 1 : 0);
+      const float2 ml = w.part_ml[slot * G + h];
+      const float* po = w.part_o + (slot * G + h) * D + lane * E;
+      float v[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[e] = po[e];
+      const float Mn = fmaxf(M, ml.x);
+      const float fo = fast_exp2(M - Mn), fn = fast_exp2(ml.x - Mn);
+      lsum = lsum * fo + ml.y * fn;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = acc[e] * fo + v[e] * fn;
+      M = Mn;
     }
+    float* op = a.out + (int64_t(rec.x) * a.hq + int64_t(cut.y) * G + h) * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) op[e] = acc[e] / lsum;
   }
 }
 
-template <bool BF16, int D, int G>
-hipError_t launch_decode_t(const AttnArgs& a, const Workspace& w, hipStream_t st) {
+template <bool BF16, int D, int G, int NBUF>
+int resident_waves() {
   static int per_cu = 0;  // resident workgroups per CU, from the occupancy calculator
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_splitk_kernel<BF16, D, G>, kDecodeThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_streamk_kernel<BF16, D, G, NBUF>, 256, 0) !=
             hipSuccess ||
         n <= 0)
       n = 1;
     per_cu = n;
   }
-  const int64_t cap = w.splits_cap * a.hkv;
-  int64_t grid = int64_t(device_cus()) * per_cu;
-  if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((decode_splitk_kernel<BF16, D, G>), dim3(unsigned(grid)), dim3(kDecodeThreads), 0, st, a, w);
+  const int waves = device_cus() * per_cu * (256 / kWave);
+  const int cap = device_cus() * kMaxWavesPerCU;
+  return waves < cap ? waves : cap;
+}
+
+template <bool BF16, int D, int G, int NBUF>
+hipError_t launch_decode_t(const AttnArgs& a, const Workspace& w, hipStream_t st) {
+  int64_t waves = resident_waves<BF16, D, G, NBUF>();
+  if (waves > w.ranges_cap) waves = w.ranges_cap;
+  const int64_t grid = (waves + 3) / 4;
+  hipLaunchKernelGGL((decode_streamk_kernel<BF16, D, G, NBUF>), dim3(unsigned(grid)), dim3(256), 0, st, a, w);
   return hipGetLastError();
 }
 
+template <int D, int G>
+hipError_t launch_merge_t(const AttnArgs& a, const Workspace& w, hipStream_t st) {
+  int64_t grid = (w.ranges_cap * G + 3) / 4;
+  if (grid > 8192) grid = 8192;
+  hipLaunchKernelGGL((split_merge_kernel<D, G>), dim3(unsigned(grid)), dim3(256), 0, st, a, w);
+  return hipGetLastError();
+}
+
+template <bool BF16, int D, int G>
+int waves_g(int nbuf) {
+  return nbuf == 2 ? resident_waves<BF16, D, G, 2>() : resident_waves<BF16, D, G, 1>();
+}
+
 template <bool BF16, int D>
-hipError_t launch_decode_d(const AttnArgs& a, const Workspace& w, int group, hipStream_t st) {
+int waves_d(int group, int nbuf) {
   switch (group) {
-    case 1: return launch_decode_t<BF16, D, 1>(a, w, st);
-    case 2: return launch_decode_t<BF16, D, 2>(a, w, st);
-    case 4: return launch_decode_t<BF16, D, 4>(a, w, st);
-    case 8: return launch_decode_t<BF16, D, 8>(a, w, st);
+    case 1: return waves_g<BF16, D, 1>(nbuf);
+    case 2: return waves_g<BF16, D, 2>(nbuf);
+    case 4: return waves_g<BF16, D, 4>(nbuf);
+    case 8: return waves_g<BF16, D, 8>(nbuf);
+    default: return 1;
+  }
+}
+
+template <bool BF16, int D, int G>
+hipError_t launch_decode_g(const AttnArgs& a, const Workspace& w, int nbuf, hipStream_t st) {
+  return nbuf == 2 ? launch_decode_t<BF16, D, G, 2>(a, w, st) : launch_decode_t<BF16, D, G, 1>(a, w, st);
+}
+
+template <bool BF16, int D>
+hipError_t launch_decode_d(const AttnArgs& a, const Workspace& w, int group, int nbuf, hipStream_t st) {
+  switch (group) {
+    case 1: return launch_decode_g<BF16, D, 1>(a, w, nbuf, st);
+    case 2: return launch_decode_g<BF16, D, 2>(a, w, nbuf, st);
+    case 4: return launch_decode_g<BF16, D, 4>(a, w, nbuf, st);
+    case 8: return launch_decode_g<BF16, D, 8>(a, w, nbuf, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_merge_d(const AttnArgs& a, const Workspace& w, int group, hipStream_t st) {
+  switch (group) {
+    case 1: return launch_merge_t<D, 1>(a, w, st);
+    case 2: return launch_merge_t<D, 2>(a, w, st);
+    case 4: return launch_merge_t<D, 4>(a, w, st);
+    case 8: return launch_merge_t<D, 8>(a, w, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const AttnArgs& a, const Workspace& w, int group, hipStream_t st) {
-  if (a.bf16) return a.d == 64 ? launch_decode_d<true, 64>(a, w, group, st) : launch_decode_d<true, 128>(a, w, group, st);
-  return a.d == 64 ? launch_decode_d<false, 64>(a, w, group, st) : launch_decode_d<false, 128>(a, w, group, st);
+int decode_buffers(int group) {
+  const int64_t v = option(PA_OPT_DECODE_BUFFERS);
+  if (v == 1 || v == 2) return int(v);
+  return group >= 8 ? 1 : 2;
 }
 
-hipError_t launch_reduce(const AttnArgs& a, const Workspace& w, int /*group*/, hipStream_t st) {
-  int64_t grid = w.rows_cap * a.hkv;
-  if (grid > 2048) grid = 2048;
-  if (a.d == 64)
-    hipLaunchKernelGGL(splitk_reduce_kernel<64>, dim3(unsigned(grid)), dim3(256), 0, st, a, w);
-  else
-    hipLaunchKernelGGL(splitk_reduce_kernel<128>, dim3(unsigned(grid)), dim3(256), 0, st, a, w);
-  return hipGetLastError();
+int decode_waves(int bf16, int head_dim, int group) {
+  const int nbuf = decode_buffers(group);
+  if (bf16) return head_dim == 64 ? waves_d<true, 64>(group, nbuf) : waves_d<true, 128>(group, nbuf);
+  return head_dim == 64 ? waves_d<false, 64>(group, nbuf) : waves_d<false, 128>(group, nbuf);
+}
+
+hipError_t launch_decode(const AttnArgs& a, const Workspace& w, int group, hipStream_t st) {
+  const int nbuf = decode_buffers(group);
+  if (a.bf16)
+    return a.d == 64 ? launch_decode_d<true, 64>(a, w, group, nbuf, st) : launch_decode_d<true, 128>(a, w, group, nbuf, st);
+  return a.d == 64 ? launch_decode_d<false, 64>(a, w, group, nbuf, st) : launch_decode_d<false, 128>(a, w, group, nbuf, st);
+}
+
+hipError_t launch_merge(const AttnArgs& a, const Workspace& w, int group, hipStream_t st) {
+  return a.d == 64 ? launch_merge_d<64>(a, w, group, st) : launch_merge_d<128>(a, w, group, st);
 }
 
 }  // namespace pa

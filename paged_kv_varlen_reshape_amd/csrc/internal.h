@@ -18,46 +18,49 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBlock = 16;         // tokens per KV block
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kDecodeThreads = 256;  // 4 waves per decode workgroup
-constexpr int kChunkRows = 32;     // query rows per MFMA chunk tile
 constexpr int kPlanThreads = 1024;
-constexpr int kMinSplitTokens = 256;   // smallest automatic split-K partition
-constexpr int kDefaultTargetItems = 8192;
+constexpr int kMaxWavesPerCU = 32;  // upper bound of resident wavefronts per CU (8 per SIMD)
 
 // ---------------------------------------------------------------- workspace
-// Plan header words (int32) at the start of the workspace.
+// Plan header words at the start of the workspace: int32 words, then int64
+// words from index H64 on.
 enum PlanHeader : int {
-  H_ROWS = 0,          // rows taking the row-wise kernel
-  H_SPLITS = 1,        // (row, split) items; decode work items = H_SPLITS * Hkv
-  H_SPLIT_TOKENS = 2,  // split-K partition P in tokens
-  H_TILES = 3,         // query tiles of the MFMA chunk kernel
-  H_REDUCE = 4,        // rows with more than one split
-  H_COUNTER = 8,       // dynamic work counter of the decode kernel
-  H_COUNTER2 = 9,      // dynamic work counter of the chunk kernel
+  H_ROWS = 0,     // row-wise rows
+  H_TILES = 1,    // query tiles of the MFMA chunk kernel
+  H_RANGES = 2,   // decode ranges (one wavefront each, in stream order)
+  H_COUNTER2 = 9, // dynamic work counter of the chunk kernel
+  H64 = 16,       // int64 words follow
+  H64_UNITS = 0,  // (row, kv head, page) units of all row-wise rows
+  H64_PER = 1,    // units per decode range
   H_WORDS = 64
 };
 
-// One (row, split) item of the row-wise kernel: query token row, sequence,
-// keys the row sees (absolute position + 1), split index | kSingleSplit.
-constexpr int kSingleSplit = 1 << 30;
-
+// Decode work is a stream of units in (row, kv head, page) order: row r owns
+// units [rows_base[r], rows_base[r] + Hkv * pages_r), kv head k of it the k-th
+// run of pages_r.  The stream is cut into ranges of equal length, one
+// wavefront each.  A (row, kv head) that a range boundary cuts leaves partial
+// results in two slots per range: slot 0 for the range's first segment, slot 1
+// for its last; split_merge folds them.
 struct Workspace {
+  int64_t* hdr64;      // hdr + H64
   int32_t* hdr;        // [H_WORDS]
-  int32_t* row_tok;    // [rows_cap]   token row of each row-wise row (plan scratch)
-  int32_t* row_seq;    // [rows_cap]
-  int32_t* row_len;    // [rows_cap]
-  int32_t* split_base; // [rows_cap+1] prefix sums of splits per row (plan scratch)
-  int4* items;         // [splits_cap] {tok, seq, len, split | kSingleSplit}
-  int4* reduce;        // [rows_cap]   {tok, first item, splits, 0} for rows with >1 split
-  int2* tiles;         // [tiles_cap]  {seq, first query row in the sequence}
-  float* part_o;       // [splits_cap * Hq * D] unnormalised split outputs
-  float2* part_ml;     // [splits_cap * Hq]     split (max, sum) in the log2 domain
-  int64_t rows_cap, tiles_cap, splits_cap;
+  int4* rows;          // [rows_cap]   {token row, seq, keys seen, 0}
+  int64_t* rows_base;  // [rows_cap]   first unit of each row
+  int2* tiles;         // [tiles_cap]  {seq, first query row of the tile within the sequence}
+  int32_t* range_row;  // [ranges_cap] row holding each range's first unit
+  int2* range_cut;     // [ranges_cap] {row, kv head} first cut by this range's start, or {-1, -1}
+  float* part_o;       // [2 * ranges_cap * G * D] unnormalised partial outputs
+  float2* part_ml;     // [2 * ranges_cap * G]     partial (max, sum), log2 domain
+  int64_t rows_cap, tiles_cap, ranges_cap;
   size_t bytes;
 };
 
 struct StepShape {
   int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq;
 };
+
+// Decode ranges the workspace must hold for this shape.
+int64_t ranges_capacity(const StepShape& s);
 
 // Carve the workspace (ws == nullptr: only compute sizes).
 Workspace layout_workspace(const StepShape& s, void* ws);
@@ -75,8 +78,9 @@ struct PlanArgs {
   int32_t num_kv_heads;
   int32_t max_len;        // max_blocks_per_seq * 16: rows never see more keys than this
   int32_t use_mfma;       // 1: sequences with >1 query rows go to the MFMA chunk kernel
-  int32_t fixed_split;    // >0: split partition in tokens
-  int32_t target_items;   // automatic split: aim at about this many (row, kv head, split) items
+  int32_t fixed_units;    // >0: units per decode range
+  int32_t num_ranges;     // automatic: spread the units over this many ranges
+  int32_t tile_rows;      // query rows per chunk-kernel tile
 };
 hipError_t launch_plan(const PlanArgs& a, const Workspace& w, hipStream_t st);
 
@@ -95,9 +99,14 @@ struct AttnArgs {
   int32_t bf16;
 };
 hipError_t launch_decode(const AttnArgs& a, const Workspace& w, int group, hipStream_t st);
-hipError_t launch_reduce(const AttnArgs& a, const Workspace& w, int group, hipStream_t st);
+// Resident decode wavefronts on the current device for this kernel instance.
+int decode_waves(int bf16, int head_dim, int group);
+// Page buffers per decode wavefront (option, else by group size).
+int decode_buffers(int group);
+hipError_t launch_merge(const AttnArgs& a, const Workspace& w, int group, hipStream_t st);
 hipError_t launch_chunk(const AttnArgs& a, const Workspace& w, int group, hipStream_t st);
 bool chunk_supported(int head_dim, int group, int bf16);
+int chunk_tile_rows(int group);
 
 int device_cus();
 

@@ -1,0 +1,94 @@
+// Ceiling kernels: streaming copy and read-only reduction over HBM.
+//
+// A grid of a few workgroups per CU walks the buffer with 16-byte lanes, each
+// thread keeping four independent loads in flight per iteration, so the
+// kernels are bound by HBM and not by issue.
+#include "internal.h"
+#include "pa_measure.h"
+
+namespace pa {
+namespace {
+
+constexpr int kMeasureThreads = 256;
+constexpr int kUnroll = 4;
+
+__global__ void __launch_bounds__(kMeasureThreads)
+copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src, int64_t n) {
+  const int64_t stride = int64_t(gridDim.x) * kMeasureThreads;
+  int64_t i = int64_t(blockIdx.x) * kMeasureThreads + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) __builtin_nontemporal_store(v[u], dst + i + u * stride);
+  }
+  for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+__global__ void __launch_bounds__(kMeasureThreads)
+read_kernel(const u32x4* __restrict__ src, int64_t n, uint32_t* __restrict__ out) {
+  __shared__ uint32_t s[kMeasureThreads / kWave];
+  const int64_t stride = int64_t(gridDim.x) * kMeasureThreads;
+  int64_t i = int64_t(blockIdx.x) * kMeasureThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) acc ^= __shfl_xor(acc, d);
+  if ((threadIdx.x & (kWave - 1)) == 0) s[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int ww = 0; ww < kMeasureThreads / kWave; ++ww) t ^= s[ww];
+    out[blockIdx.x] = t;
+  }
+}
+
+int measure_grid() {
+  const int g = device_cus() * 8;
+  return g < 65536 ? g : 65536;
+}
+
+int check(const void* a, const void* b, size_t bytes, const char* who) {
+  if (!a || !b) return fail(PA_ERR_INVALID, "%s: null pointer", who);
+  if (bytes == 0 || bytes % 16 != 0) return fail(PA_ERR_INVALID, "%s: bytes must be a positive multiple of 16", who);
+  if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) % 16 != 0)
+    return fail(PA_ERR_INVALID, "%s: pointers must be 16-byte aligned", who);
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" int pa_measure_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  clear_error();
+  if (int rc = check(dst, src, bytes, "pa_measure_copy")) return rc;
+  const char* s = static_cast<const char*>(src);
+  const char* d = static_cast<const char*>(dst);
+  if (s < d + bytes && d < s + bytes) return fail(PA_ERR_INVALID, "pa_measure_copy: buffers overlap");
+  hipLaunchKernelGGL(copy_kernel, dim3(measure_grid()), dim3(kMeasureThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), int64_t(bytes / 16));
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : fail(PA_ERR_HIP, "pa_measure_copy: launch failed: %s", hipGetErrorString(e));
+}
+
+extern "C" int pa_measure_read(const void* src, size_t bytes, uint32_t* out, void* stream) {
+  clear_error();
+  if (int rc = check(src, out, bytes, "pa_measure_read")) return rc;
+  hipLaunchKernelGGL(read_kernel, dim3(measure_grid()), dim3(kMeasureThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), int64_t(bytes / 16), out);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : fail(PA_ERR_HIP, "pa_measure_read: launch failed: %s", hipGetErrorString(e));
+}

@@ -5,15 +5,17 @@
 // section "PagedAttentionの仕組み") that mixes prefill chunks and single-token
 // decodes (section "エンジンの中核：スケジューラとKVキャッシュ管理").  Each
 // sequence's query rows go either to the MFMA chunk kernel (bf16 sequences
-// with more than one query row, in tiles of kChunkRows rows) or to the
-// row-wise split-K kernel (decodes, and every row when MFMA is off).  A
-// row-wise row at absolute position p sees p+1 keys; it is cut into splits of
-// P tokens, P chosen so that the whole step makes about `target_items`
-// (row, kv head, split) items, never below kMinSplitTokens.
+// with more than one query row, in tiles of `tile_rows` rows) or to the
+// row-wise decode kernel (decodes, and every row when MFMA is off).  A
+// row-wise row at absolute position p sees p+1 keys, i.e. ceil((p+1)/16)
+// pages per kv head; all those (row, kv head, page) units form one stream
+// that is cut into equal ranges, one per decode wavefront.
 //
-// One workgroup of 1024 threads walks the sequences, then the rows, in chunks
-// of 1024 with block-wide scans.  It also clears the work counters the later
-// kernels of the step use.
+// One workgroup of 1024 threads.  Pass 1 walks the sequences in chunks of
+// 1024 with block scans that place every tile record, row record and row's
+// first unit; pass 2 walks the rows and marks, for every range, the row
+// holding its first unit and the (row, kv head) it cuts.  It also clears the
+// work counter the chunk kernel uses.
 #include "internal.h"
 
 namespace pa {
@@ -21,123 +23,146 @@ namespace {
 
 constexpr int kWavesPerPlan = kPlanThreads / kWave;
 
-// Exclusive scan over the workgroup; returns this thread's prefix, total in *total.
-__device__ int64_t block_exclusive_scan(int64_t x, int64_t* total, int64_t* sh) {
+// Exclusive scans of two non-negative int64 at once (one set of barriers).
+__device__ void block_exclusive_scan2(int64_t x, int64_t y, int64_t* ox, int64_t* oy, int64_t* tx, int64_t* ty,
+                                      int64_t* sh) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  int64_t inc = x;
+  int64_t ix = x, iy = y;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
-    const int64_t y = __shfl_up(inc, d);
-    if (lane >= d) inc += y;
-  }
-  if (lane == kWave - 1) sh[wave] = inc;
-  __syncthreads();
-  if (wave == 0) {
-    int64_t w = lane < kWavesPerPlan ? sh[lane] : 0;
-#pragma unroll
-    for (int d = 1; d < kWavesPerPlan; d <<= 1) {
-      const int64_t y = __shfl_up(w, d);
-      if (lane >= d) w += y;
+    const int64_t a = __shfl_up(ix, d), b = __shfl_up(iy, d);
+    if (lane >= d) {
+      ix += a;
+      iy += b;
     }
-    if (lane < kWavesPerPlan) sh[kWavesPerPlan + lane] = w;  // inclusive wave prefix
+  }
+  if (lane == kWave - 1) {
+    sh[wave] = ix;
+    sh[kWavesPerPlan + wave] = iy;
   }
   __syncthreads();
-  const int64_t before = wave ? sh[kWavesPerPlan + wave - 1] : 0;
-  *total = sh[2 * kWavesPerPlan - 1];
+  int64_t bx = 0, by = 0, sx = 0, sy = 0;
+#pragma unroll
+  for (int ww = 0; ww < kWavesPerPlan; ++ww) {
+    const int64_t vx = sh[ww], vy = sh[kWavesPerPlan + ww];
+    bx += ww < wave ? vx : 0;
+    by += ww < wave ? vy : 0;
+    sx += vx;
+    sy += vy;
+  }
+  *ox = bx + ix - x;
+  *oy = by + iy - y;
+  *tx = sx;
+  *ty = sy;
   __syncthreads();
-  return before + inc - x;
+}
+
+// Units (pages of 16 keys) of the rows whose key counts are 1..n:
+// sum over p = 1..n of ceil(p / 16).
+__device__ __forceinline__ int64_t pages_upto(int64_t n) {
+  const int64_t a = n / kBlock, b = n - a * kBlock;
+  return kBlock * a * (a + 1) / 2 + b * (a + 1);
+}
+
+struct SeqInfo {
+  int32_t r0, q, c;
+  bool chunk;
+};
+
+__device__ __forceinline__ SeqInfo seq_info(const PlanArgs& a, int i) {
+  SeqInfo s{0, 0, 0, false};
+  if (i >= a.num_seqs) return s;
+  int32_t r0 = a.qsl[i];
+  int32_t q = a.qsl[i + 1] - r0;
+  int32_t c = a.ctx[i];
+  // metadata is trusted, but nothing below may index outside the arrays
+  if (q < 0) q = 0;
+  if (r0 < 0 || r0 >= a.num_tokens) q = 0;
+  if (q > a.num_tokens - r0) q = a.num_tokens - r0;
+  if (c < 0) c = 0;
+  if (int64_t(c) + q > a.max_len) q = c >= a.max_len ? 0 : a.max_len - c;
+  s.r0 = r0;
+  s.q = q;
+  s.c = c;
+  s.chunk = q > 1 && a.use_mfma;
+  return s;
 }
 
 __global__ void __launch_bounds__(kPlanThreads)
 plan_kernel(PlanArgs a, Workspace w) {
   __shared__ int64_t sh[2 * kWavesPerPlan];
   const int tid = threadIdx.x;
-  int64_t rows = 0, tiles = 0, keys = 0;
+  const int64_t hkv = a.num_kv_heads;
 
-  // pass 1: rows and tiles of every sequence
+  // pass 1: scans place the tile records, the row records (packed high/low
+  // words of one value) and each row's first unit
+  int64_t tiles = 0, rows = 0, units = 0;
   for (int base = 0; base < a.num_seqs; base += kPlanThreads) {
     const int i = base + tid;
-    int64_t nrow = 0, ntile = 0, nkey = 0;
-    int32_t q = 0, c = 0, r0 = 0;
-    if (i < a.num_seqs) {
-      r0 = a.qsl[i];
-      q = a.qsl[i + 1] - r0;
-      c = a.ctx[i];
-      // metadata is trusted, but nothing below may index outside the arrays
-      if (q < 0) q = 0;
-      if (r0 < 0 || r0 >= a.num_tokens) q = 0;
-      if (q > a.num_tokens - r0) q = a.num_tokens - r0;
-      if (c < 0) c = 0;
-      if (int64_t(c) + q > a.max_len) q = c >= a.max_len ? 0 : a.max_len - c;
-      if (q > 1 && a.use_mfma) {
-        ntile = (q + kChunkRows - 1) / kChunkRows;
-      } else if (q > 0) {
-        nrow = q;
-        nkey = int64_t(q) * c + int64_t(q) * (q + 1) / 2;
-      }
+    const SeqInfo s = seq_info(a, i);
+    int64_t ntile = 0, nrow = 0, nunit = 0;
+    if (s.chunk) {
+      ntile = (s.q + a.tile_rows - 1) / a.tile_rows;
+    } else if (s.q > 0) {
+      nrow = s.q;
+      nunit = hkv * (pages_upto(int64_t(s.c) + s.q) - pages_upto(s.c));
     }
-    int64_t tot_r, tot_t, tot_k;
-    const int64_t off_r = rows + block_exclusive_scan(nrow, &tot_r, sh);
-    const int64_t off_t = tiles + block_exclusive_scan(ntile, &tot_t, sh);
-    block_exclusive_scan(nkey, &tot_k, sh);
-    for (int64_t j = 0; j < nrow && off_r + j < w.rows_cap; ++j) {
-      w.row_tok[off_r + j] = r0 + int32_t(j);
-      w.row_seq[off_r + j] = i;
-      w.row_len[off_r + j] = c + int32_t(j) + 1;
+    int64_t off_tr, off_u, tot_tr, tot_u;
+    block_exclusive_scan2((ntile << 32) | nrow, nunit, &off_tr, &off_u, &tot_tr, &tot_u, sh);
+    const int64_t t0 = tiles + (off_tr >> 32), r0 = rows + (off_tr & 0xFFFFFFFFll);
+    // longest tiles of a sequence first: they see the most keys
+    for (int64_t t = 0; t < ntile && t0 + t < w.tiles_cap; ++t)
+      w.tiles[t0 + t] = make_int2(i, int32_t(ntile - 1 - t) * a.tile_rows);
+    int64_t u = units + off_u;
+    for (int32_t j = 0; j < nrow && r0 + j < w.rows_cap; ++j) {
+      const int32_t len = s.c + j + 1;
+      w.rows[r0 + j] = make_int4(s.r0 + j, i, len, 0);
+      w.rows_base[r0 + j] = u;
+      u += hkv * ((len + kBlock - 1) / kBlock);
     }
-    for (int64_t t = 0; t < ntile && off_t + t < w.tiles_cap; ++t)
-      w.tiles[off_t + t] = make_int2(i, int32_t(t) * kChunkRows);
-    rows += tot_r;
-    tiles += tot_t;
-    keys += tot_k;
+    tiles += tot_tr >> 32;
+    rows += tot_tr & 0xFFFFFFFFll;
+    units += tot_u;
   }
-
-  // split partition
-  int64_t P;
-  if (a.fixed_split > 0) {
-    P = a.fixed_split;
-  } else {
-    const int64_t want = (keys * a.num_kv_heads + a.target_items - 1) / a.target_items;
-    P = (want + kBlock - 1) / kBlock * kBlock;
-    if (P < kMinSplitTokens) P = kMinSplitTokens;
-    if (P > (int64_t(1) << 30)) P = int64_t(1) << 30;
-  }
+  if (tiles > w.tiles_cap) tiles = w.tiles_cap;  // only with inconsistent metadata
   if (rows > w.rows_cap) rows = w.rows_cap;
-  if (tiles > w.tiles_cap) tiles = w.tiles_cap;
-  __syncthreads();  // row_* written above are read by other threads below
 
-  // pass 2: splits per row, item records, reduce list
-  int64_t splits = 0, nred = 0;
-  for (int base = 0; base < rows; base += kPlanThreads) {
-    const int64_t r = base + tid;
-    int64_t ns = 0;
-    int32_t tok = 0, seq = 0, len = 0;
-    if (r < rows) {
-      tok = w.row_tok[r];
-      seq = w.row_seq[r];
-      len = w.row_len[r];
-      ns = (len + P - 1) / P;
+  // the unit stream is cut into ranges of `per` units
+  int64_t per = a.fixed_units > 0 ? a.fixed_units : (units + a.num_ranges - 1) / a.num_ranges;
+  if (per < 1) per = 1;
+  int64_t nranges = (units + per - 1) / per;
+  if (nranges > w.ranges_cap) {  // a fixed range length too short for the workspace
+    per = (units + w.ranges_cap - 1) / w.ranges_cap;
+    nranges = (units + per - 1) / per;
+  }
+  __syncthreads();  // row records written above are read by other threads below
+
+  // pass 2, one thread per (row, kv head): every range start names the row
+  // holding it and, if it is the first boundary inside the pair, the pair
+  const double inv_per = 1.0 / double(per);
+  for (int64_t pr = tid; pr < rows * hkv; pr += kPlanThreads) {
+    const int64_t r = pr / hkv;
+    const int k = int(pr - r * hkv);
+    const int64_t pages = (w.rows[r].z + kBlock - 1) / kBlock;
+    const int64_t start = w.rows_base[r] + k * pages;  // first unit of (r, k)
+    // first range whose start lies in [start, start + pages)
+    int64_t g = int64_t(double(start) * inv_per);
+    while (g * per < start) ++g;
+    while (g > 0 && (g - 1) * per >= start) --g;
+    for (; g * per < start + pages && g < nranges; ++g) {
+      const bool cut = g * per > start && (g - 1) * per <= start;  // first boundary strictly inside
+      w.range_row[g] = int32_t(r);
+      w.range_cut[g] = cut ? make_int2(int32_t(r), k) : make_int2(-1, -1);
     }
-    int64_t tot_s, tot_red;
-    const int64_t u0 = splits + block_exclusive_scan(ns, &tot_s, sh);
-    const int64_t red = nred + block_exclusive_scan(ns > 1 ? 1 : 0, &tot_red, sh);
-    for (int64_t s = 0; s < ns && u0 + s < w.splits_cap; ++s)
-      w.items[u0 + s] = make_int4(tok, seq, len, int32_t(s) | (ns == 1 ? kSingleSplit : 0));
-    if (ns > 1 && u0 + ns <= w.splits_cap) w.reduce[red] = make_int4(tok, int32_t(u0), int32_t(ns), 0);
-    splits += tot_s;
-    nred += tot_red;
   }
 
-  if (splits > w.splits_cap) splits = w.splits_cap;  // only with inconsistent metadata
-  if (nred > w.rows_cap) nred = w.rows_cap;
   if (tid == 0) {
     w.hdr[H_ROWS] = int32_t(rows);
-    w.hdr[H_SPLITS] = int32_t(splits);
-    w.hdr[H_SPLIT_TOKENS] = int32_t(P);
     w.hdr[H_TILES] = int32_t(tiles);
-    w.hdr[H_REDUCE] = int32_t(nred);
-    w.hdr[H_COUNTER] = 0;
+    w.hdr[H_RANGES] = int32_t(nranges);
     w.hdr[H_COUNTER2] = 0;
+    w.hdr64[H64_UNITS] = units;
+    w.hdr64[H64_PER] = per;
   }
 }
 

@@ -15,22 +15,25 @@
 namespace pa {
 namespace {
 
+// Thread c moves chunk c & (cpr-1) of source row c >> cpr_log2, where a source
+// row is one (token, kv head) pair; cpr (16-byte chunks per row) is 8, 16 or 32.
 __global__ void __launch_bounds__(256)
 reshape_and_cache_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
                          const int32_t* __restrict__ slots, u32x4* __restrict__ kc,
-                         u32x4* __restrict__ vc, int64_t total_chunks, int32_t hkv,
-                         int32_t chunks_per_row, int64_t num_slots) {
-  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; c < total_chunks; c += stride) {
-    const int64_t row = c / chunks_per_row;        // token * hkv + head
-    const int32_t part = int32_t(c - row * chunks_per_row);
-    const int64_t tok = row / hkv;
-    const int32_t head = int32_t(row - tok * hkv);
+                         u32x4* __restrict__ vc, uint32_t total_chunks, uint32_t hkv,
+                         uint32_t cpr_log2, int64_t num_slots) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  const uint32_t cpr_mask = (1u << cpr_log2) - 1;
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < total_chunks; c += stride) {
+    const uint32_t row = c >> cpr_log2;  // token * hkv + head
+    const uint32_t part = c & cpr_mask;
+    const uint32_t tok = row / hkv;
+    const uint32_t head = row - tok * hkv;
     const int32_t slot = slots[tok];
     if (slot < 0 || slot >= num_slots) continue;  // negative: skip; past the pool: never written
     const int64_t block = slot >> 4;
     const int32_t off = slot & (kBlock - 1);
-    const int64_t dst = ((block * hkv + head) * kBlock + off) * chunks_per_row + part;
+    const int64_t dst = (((block * hkv + head) * kBlock + off) << cpr_log2) + part;
     const u32x4 kk = __builtin_nontemporal_load(k + c);
     const u32x4 vv = __builtin_nontemporal_load(v + c);
     kc[dst] = kk;
@@ -43,14 +46,15 @@ reshape_and_cache_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, const int32_t* slots, void* kc,
                                     void* vc, int32_t ntok, int32_t hkv, int32_t row_bytes,
                                     int64_t num_blocks, hipStream_t st) {
-  const int32_t cpr = row_bytes / 16;
-  const int64_t total = int64_t(ntok) * hkv * cpr;
+  const uint32_t cpr = uint32_t(row_bytes / 16);
+  const uint32_t cpr_log2 = uint32_t(__builtin_ctz(cpr));
+  const int64_t total = int64_t(ntok) * hkv * cpr;  // < 2^31, checked by the caller
   const int64_t want = (total + 255) / 256;
   const int blocks = int(want < 65536 ? want : 65536);
   hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(blocks), dim3(256), 0, st,
                      static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), slots,
-                     static_cast<u32x4*>(kc), static_cast<u32x4*>(vc), total, hkv, cpr,
-                     num_blocks * kBlock);
+                     static_cast<u32x4*>(kc), static_cast<u32x4*>(vc), uint32_t(total), uint32_t(hkv),
+                     cpr_log2, num_blocks * kBlock);
   return hipGetLastError();
 }
 

@@ -14,10 +14,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def header_functions():
-    src = open(os.path.join(ROOT, "include", "pa.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", src)
-    return sorted(set(names))
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            src = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, h)).read(), flags=re.S)
+            names.update(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -33,8 +36,13 @@ def test_binding_covers_header():
     assert set(header_functions()) == set(B.SIGNATURES)
 
 
-def _rc(call):
-    return call
+def test_measure_rejects_bad_arguments():
+    lib = pk.lib()
+    assert lib.pa_measure_copy(16, 4096, 100, None) == pk.PA_ERR_INVALID  # not a multiple of 16
+    assert lib.pa_measure_copy(16, 32, 64, None) == pk.PA_ERR_INVALID  # overlap
+    assert lib.pa_measure_copy(None, 32, 64, None) == pk.PA_ERR_INVALID
+    assert lib.pa_measure_read(8, 64, 4096, None) == pk.PA_ERR_INVALID  # misaligned
+    assert lib.pa_measure_read(16, 0, 4096, None) == pk.PA_ERR_INVALID
 
 
 def test_reshape_rejects_bad_arguments():
