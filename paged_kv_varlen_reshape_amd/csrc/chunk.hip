@@ -1,9 +1,332 @@
 // chunk_mfma: causal attention of multi-row (prefill chunk) sequences on bf16 MFMA.
-// Not built yet: every row takes the row-wise kernel.
+//
+// Prefill processes every prompt token of a request at once and is bound by
+// compute (Inside vLLM summary, techfeed.io, section "エンジンの中核：スケジューラ
+// とKVキャッシュ管理"); long prompts arrive as chunks on top of tokens already
+// cached (section "高度な機能群", chunked prefill), and each chunk row attends
+// only to its own sequence's keys up to its own position (section
+// "PagedAttentionの仕組み": flattened super-sequence with positions and mask).
+// Row j of a chunk with c cached tokens sits at position p = c + j and sees
+// keys 0..p, read through the block table.
+//
+// Tile: 128 query rows = (128/G tokens) x (the G query heads of one kv head),
+// so one K/V tile in LDS serves the whole GQA group.  Wavefront w owns rows
+// 32w..32w+31 (row rho = head_in_group * TQ + token).  Keys come in tiles of 64
+// (four 16-token pages).  Both products run transposed on
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
+//   S^T[key][row] = sum_d K[key][d] Q[row][d]        (A = K from LDS, B = Q in registers)
+//   O^T[d][row]  += sum_key V^T[d][key] P^T[key][row] (A = V^T from LDS, B = P in registers)
+// In the 32x32 accumulator layout lane l holds column l%32 (one query row) and
+// 16 rows (keys), so a query row's max and sum need only one exchange between
+// lanes l and l^32, and the bf16 weights P feed the PV product straight from
+// the S^T accumulator: the PV operand slots are matched to the keys the lane
+// holds, and V^T is read from LDS in the same key order.
+//
+// Online softmax in the log2 domain on the VALU; P is rounded to bf16 for the
+// PV product and the row sum l adds the rounded values, so the output is an
+// exact convex combination of V rows with the rounded weights.  Keys past a
+// row's position get -inf by select; K and V of keys past the tile's last
+// position are written to LDS as zeros and never read from the pool, so
+// nothing outside the sequence reaches the products (NaN-safe).
+//
+// Staging: 256 threads load one 64-key tile of K and V (16 bytes per load, a
+// fully used 256-byte row segment per 16 lanes); K goes to LDS row-major, V is
+// transposed in registers (4 keys x 8 dims per thread) and written as V^T.  The
+// next tile's page ids and K/V loads are in flight while the current tile is
+// multiplied.  Tiles are taken from a work counter, longest first within a
+// sequence.
 #include "internal.h"
 
 namespace pa {
-bool chunk_supported(int, int, int) { return false; }
-int chunk_tile_rows(int) { return 32; }
-hipError_t launch_chunk(const AttnArgs&, const Workspace&, int, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kTileRows = 128;  // query rows per workgroup tile
+constexpr int kBN = 64;         // keys per K/V tile
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// two floats -> two bf16 (round to nearest even) in one dword
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2_t h = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int D>
+struct ChunkCfg {
+  static constexpr int KSTEPS = D / 16;            // MFMA k-steps of Q.K (16 dims each)
+  static constexpr int DBLK = D / 32;              // 32-dim blocks of O^T
+  static constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
+  static constexpr int KPT = kBN * CPR / kThreads; // keys staged per thread: 4 (D=128) or 2 (D=64)
+  static constexpr int KS = D + 8;                 // LDS row stride of K (elements), padded
+  static constexpr int VS = kBN + 8;               // LDS row stride of V^T (elements), padded
+  static_assert(KPT == 2 || KPT == 4, "staging layout");
+};
+
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads, 2)
+chunk_mfma_kernel(AttnArgs a, Workspace w) {
+  using C = ChunkCfg<D>;
+  constexpr int KSTEPS = C::KSTEPS, DBLK = C::DBLK, CPR = C::CPR, KPT = C::KPT, KS = C::KS, VS = C::VS;
+  constexpr int TQ = kTileRows / G;  // tokens per tile
+  constexpr int ROW_BYTES = D * 2;
+
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[kBN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * VS];
+  __shared__ int s_item;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int col = lane & 31;  // accumulator column = query row within the wavefront
+  const int lg = lane >> 5;   // lane half
+  // staging coordinates: 16-byte chunk of a row, and the first of KPT keys
+  const int sc = tid % CPR;
+  const int sk = (tid / CPR) * KPT;
+
+  const int n_items = w.hdr[H_TILES] * a.hkv;
+  const int64_t page_stride = int64_t(kBlock) * ROW_BYTES;
+  const char* kbase = static_cast<const char*>(a.kc);
+  const char* vbase = static_cast<const char*>(a.vc);
+
+  if (tid == 0) s_item = blockIdx.x;
+  __syncthreads();
+  int item = s_item;
+  while (item < n_items) {
+    __syncthreads();  // every thread has read s_item
+    if (tid == 0) s_item = int(gridDim.x) + atomicAdd(&w.hdr[H_COUNTER2], 1);
+
+    const int tile = item / a.hkv;
+    const int kvh = item - tile * a.hkv;
+    const int2 trec = w.tiles[tile];
+    const int seq = trec.x, t0 = trec.y;
+    const int r0 = a.qsl[seq];
+    const int ctx = max(a.ctx[seq], 0);
+    // the plan clamped the rows it tiled the same way: nothing may index
+    // outside q, out or the block-table row even with inconsistent metadata
+    const int qlen = min(min(a.qsl[seq + 1] - r0, a.num_tokens - r0), a.mbps * kBlock - ctx);
+    const int nt = max(0, min(TQ, qlen - t0));  // valid tokens of this tile
+    const int kv_end = ctx + t0 + nt;   // keys seen by the tile's last row
+    const int n_kt = (kv_end + kBN - 1) / kBN;
+    const int n_pages = (kv_end + kBlock - 1) / kBlock;
+    const int32_t* btrow = a.bt + int64_t(seq) * a.mbps;
+
+    // this lane's query row
+    const int rho = wave * 32 + col;
+    const int hh = rho / TQ, tt = rho - hh * TQ;
+    const bool valid = tt < nt;
+    const int pos = ctx + t0 + tt;  // keys 0..pos are visible
+    const int head = kvh * G + hh;
+
+    u32x4 qf[KSTEPS];
+    {
+      const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) +
+                                                       ((int64_t(r0) + t0 + tt) * a.hq + head) * ROW_BYTES);
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = valid ? qp[2 * kk + lg] : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    f32x16_t o[DBLK];
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) o[db] = f32x16_t{};
+    float m = -INFINITY, l = 0.f;
+
+    // staging registers: KPT keys x one 16-byte chunk of K and of V
+    u32x4 gk[KPT], gv[KPT];
+    auto page_id = [&](int kt) -> int32_t {
+      const int page = (kt * kBN + sk) / kBlock;
+      int32_t b = page < n_pages ? btrow[page] : 0;
+      return b < 0 ? 0 : (b >= a.nb ? int32_t(a.nb - 1) : b);
+    };
+    auto load_tile = [&](int kt, int32_t blk) {
+      const int key = kt * kBN + sk;
+      const int64_t off = (int64_t(blk) * a.hkv + kvh) * page_stride + int64_t(key % kBlock) * ROW_BYTES + sc * 16;
+      const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + off);
+      const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + off);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const bool in = key + i < kv_end;
+        gk[i] = in ? kp[i * (ROW_BYTES / 16)] : u32x4{0u, 0u, 0u, 0u};
+        gv[i] = in ? vp[i * (ROW_BYTES / 16)] : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+
+    int32_t id_next = page_id(0);
+    load_tile(0, id_next);
+    if (n_kt > 1) id_next = page_id(1);
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+      __syncthreads();  // the previous tile's LDS reads are done
+      // K row-major
+#pragma unroll
+      for (int i = 0; i < KPT; ++i)
+        *reinterpret_cast<u32x4*>(&s_k[(sk + i) * KS + sc * 8]) = gk[i];
+      // V transposed: for each of the 8 dims of the chunk, KPT consecutive keys
+      {
+        uint32_t wv[KPT][4];
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+          wv[i][0] = gv[i].x; wv[i][1] = gv[i].y; wv[i][2] = gv[i].z; wv[i][3] = gv[i].w;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int dw = e >> 1;
+          const bool hi = e & 1;
+          uint16_t* dst = &s_vt[(sc * 8 + e) * VS + sk];
+          if constexpr (KPT == 4) {
+            const uint32_t a0 = hi ? (wv[0][dw] >> 16) | (wv[1][dw] & 0xFFFF0000u)
+                                   : (wv[0][dw] & 0xFFFFu) | (wv[1][dw] << 16);
+            const uint32_t a1 = hi ? (wv[2][dw] >> 16) | (wv[3][dw] & 0xFFFF0000u)
+                                   : (wv[2][dw] & 0xFFFFu) | (wv[3][dw] << 16);
+            *reinterpret_cast<uint2*>(dst) = make_uint2(a0, a1);
+          } else {
+            const uint32_t a0 = hi ? (wv[0][dw] >> 16) | (wv[1][dw] & 0xFFFF0000u)
+                                   : (wv[0][dw] & 0xFFFFu) | (wv[1][dw] << 16);
+            *reinterpret_cast<uint32_t*>(dst) = a0;
+          }
+        }
+      }
+      __syncthreads();  // tile kt is in LDS
+
+      // next tile's loads fly while this one is multiplied
+      if (kt + 1 < n_kt) {
+        load_tile(kt + 1, id_next);
+        if (kt + 2 < n_kt) id_next = page_id(kt + 2);
+      }
+
+      const int key0 = kt * kBN;
+      // S^T = K Q^T: two 32-key blocks
+      f32x16_t s[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        s[mb] = f32x16_t{};
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(&s_k[(mb * 32 + col) * KS + kk * 16 + lg * 8]);
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[kk]), s[mb], 0, 0, 0);
+        }
+      }
+      // causal mask (also hides keys past the tile's end): key > pos -> -inf
+      if (key0 + kBN - 1 > ctx + t0) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = key0 + mb * 32 + (j / 4) * 8 + lg * 4 + (j % 4);
+            if (key > pos) s[mb][j] = -INFINITY;
+          }
+      }
+      // online softmax for this lane's row (scores scaled into the log2 domain)
+      float mx = s[0][0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[0][j]);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[1][j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m, mx * a.scale_log2);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m - m_use);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
+
+      // P^T in bf16 pairs: pk[mb][i] holds keys j = 2i, 2i+1 of block mb
+      uint32_t pk[2][8];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p0 = fast_exp2(fmaf(s[mb][2 * i], a.scale_log2, -m_use));
+          const float p1 = fast_exp2(fmaf(s[mb][2 * i + 1], a.scale_log2, -m_use));
+          pk[mb][i] = pack_bf16(p0, p1);
+          l += bf16lo(pk[mb][i]) + bf16hi(pk[mb][i]);
+        }
+
+      // O^T += V^T P^T: four 16-key steps; step t uses accumulator rows
+      // j = (t%2)*8 .. +8 of block t/2, i.e. keys 16t + (i/4)*8 + lg*4 + i%4
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const u32x4 pb = {pk[t / 2][(t % 2) * 4 + 0], pk[t / 2][(t % 2) * 4 + 1], pk[t / 2][(t % 2) * 4 + 2],
+                          pk[t / 2][(t % 2) * 4 + 3]};
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          const uint16_t* vrow = &s_vt[(db * 32 + col) * VS + 16 * t + lg * 4];
+          const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8);
+          const u32x4 va = {v0.x, v0.y, v1.x, v1.y};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb), o[db], 0, 0, 0);
+        }
+      }
+    }
+
+    // the two lane halves hold disjoint keys of the same row
+    l += __shfl_xor(l, 32);
+    if (valid) {
+      const float inv = 1.f / l;
+      float* op = a.out + ((int64_t(r0) + t0 + tt) * a.hq + head) * D;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          const float4 v = make_float4(o[db][jb * 4 + 0] * inv, o[db][jb * 4 + 1] * inv, o[db][jb * 4 + 2] * inv,
+                                       o[db][jb * 4 + 3] * inv);
+          *reinterpret_cast<float4*>(op + db * 32 + jb * 8 + lg * 4) = v;
+        }
+    }
+
+    __syncthreads();
+    item = s_item;
+  }
+}
+
+template <int D, int G>
+hipError_t launch_chunk_t(const AttnArgs& a, const Workspace& w, hipStream_t st) {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_mfma_kernel<D, G>, kThreads, 0) != hipSuccess || n <= 0)
+      n = 1;
+    per_cu = n;
+  }
+  int64_t grid = int64_t(device_cus()) * per_cu;
+  const int64_t cap = w.tiles_cap * a.hkv;
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL((chunk_mfma_kernel<D, G>), dim3(unsigned(grid)), dim3(kThreads), 0, st, a, w);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_chunk_d(const AttnArgs& a, const Workspace& w, int group, hipStream_t st) {
+  switch (group) {
+    case 1: return launch_chunk_t<D, 1>(a, w, st);
+    case 2: return launch_chunk_t<D, 2>(a, w, st);
+    case 4: return launch_chunk_t<D, 4>(a, w, st);
+    case 8: return launch_chunk_t<D, 8>(a, w, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool chunk_supported(int head_dim, int group, int bf16) {
+  return bf16 && (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+int chunk_tile_rows(int group) { return kTileRows / group; }
+
+hipError_t launch_chunk(const AttnArgs& a, const Workspace& w, int group, hipStream_t st) {
+  return a.d == 64 ? launch_chunk_d<64>(a, w, group, st) : launch_chunk_d<128>(a, w, group, st);
+}
+
 }  // namespace pa
