@@ -102,6 +102,28 @@ def measure_ceilings(pk, torch, reps: int = 10):
     return dict(copy_GBps=copy_gbs, read_GBps=read_gbs)
 
 
+def recorded_traffic(kernel: str, cfg_id: int):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled against a copy of known
+    size) recorded under profiles/ for this kernel and workload, or None if there is
+    no record or the kernel's sources changed since the counters were taken."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("decode.hip", "plan.hip", "internal.h"):
+        with open(os.path.join(ROOT, "paged_kv_varlen_reshape_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    sha = h.hexdigest()[:16]
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*.traffic.txt")):
+        for line in open(path):
+            if not line.startswith("traffic:"):
+                continue
+            kv = dict(x.split("=", 1) for x in line.split()[1:])
+            if kv.get("kernel") == kernel and kv.get("config") == str(cfg_id) and kv.get("src_sha") == sha:
+                return int(kv["fetch_bytes"]) + int(kv["write_bytes"])
+    return None
+
+
 def cpu_baseline(spec, seconds: float):
     """The fp64 oracle timed on this host's cores over a bounded sample of the workload."""
     import numpy as np
@@ -231,7 +253,8 @@ def main(argv=None):
     else:
         ach = work["decode_kernel_bytes"] / (decode_avg * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS,
-                    traffic=None, kernel="decode_streamk", kernel_avg_us=decode_avg * 1e3)
+                    traffic=recorded_traffic("decode_streamk", spec.cfg_id), kernel="decode_streamk",
+                    kernel_avg_us=decode_avg * 1e3, algorithmic_bytes=work["decode_kernel_bytes"])
         if ceil:
             roof["frac_of_measured_copy"] = ach / ceil["copy_GBps"]
             roof["frac_of_measured_read"] = ach / ceil["read_GBps"]

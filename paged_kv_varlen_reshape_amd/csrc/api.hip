@@ -114,6 +114,7 @@ Workspace layout_workspace(const StepShape& s, void* ws) {
   w.rows = reinterpret_cast<int4*>(take(w.rows_cap * sizeof(int4)));
   w.rows_base = reinterpret_cast<int64_t*>(take(w.rows_cap * sizeof(int64_t)));
   w.tiles = reinterpret_cast<int2*>(take(w.tiles_cap * sizeof(int2)));
+  w.tiles_tmp = reinterpret_cast<int4*>(take(w.tiles_cap * sizeof(int4)));
   w.range_row = reinterpret_cast<int32_t*>(take(w.ranges_cap * sizeof(int32_t)));
   w.range_cut = reinterpret_cast<int2*>(take(w.ranges_cap * sizeof(int2)));
   w.part_o = reinterpret_cast<float*>(take(size_t(2 * w.ranges_cap * G) * s.head_dim * sizeof(float)));

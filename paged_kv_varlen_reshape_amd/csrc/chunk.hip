@@ -31,10 +31,15 @@
 //
 // Staging: 256 threads load one 64-key tile of K and V (16 bytes per load, a
 // fully used 256-byte row segment per 16 lanes); K goes to LDS row-major, V is
-// transposed in registers (4 keys x 8 dims per thread) and written as V^T.  The
-// next tile's page ids and K/V loads are in flight while the current tile is
-// multiplied.  Tiles are taken from a work counter, longest first within a
-// sequence.
+// transposed in registers (4 keys x 8 dims per thread) and written as V^T
+// (bank-conflict-free layout, see the V^T layout note).  LDS holds two tiles: while tile
+// kt is multiplied, tile kt+1 (loaded during tile kt-1) is staged into the
+// other buffer and the loads of tile kt+2 are issued, with one barrier per
+// tile.  The reference maximum of the online softmax moves lazily, so the O
+// accumulators are rescaled only when a row's maximum grows by more than 2^8.
+// Tiles are taken from a work counter, longest first within a sequence.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace pa {
@@ -62,6 +67,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// LDS layout of V^T[d][key]: rows are VS elements apart and the 8-byte key
+// groups of row d (four keys each) are permuted by XOR with d/16, i.e. group
+// u of row d sits at element d*VS + 4*(u ^ (d>>4)).  With VS = 68 both the
+// staging stores (16 lanes: rows 8 apart, one key group) and the operand loads
+// (16 lanes: consecutive rows, one key group) touch 32 distinct banks.
+
+constexpr bf16x2_t kOnes = {__bf16(1.0f), __bf16(1.0f)};
+
 template <int D>
 struct ChunkCfg {
   static constexpr int KSTEPS = D / 16;            // MFMA k-steps of Q.K (16 dims each)
@@ -69,7 +82,7 @@ struct ChunkCfg {
   static constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
   static constexpr int KPT = kBN * CPR / kThreads; // keys staged per thread: 4 (D=128) or 2 (D=64)
   static constexpr int KS = D + 8;                 // LDS row stride of K (elements), padded
-  static constexpr int VS = kBN + 8;               // LDS row stride of V^T (elements), padded
+  static constexpr int VS = kBN + 4;               // LDS row stride of V^T (elements), padded
   static_assert(KPT == 2 || KPT == 4, "staging layout");
 };
 
@@ -81,8 +94,9 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
   constexpr int TQ = kTileRows / G;  // tokens per tile
   constexpr int ROW_BYTES = D * 2;
 
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kBN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * VS];
+  // two buffers each: the next tile is staged while this one is multiplied
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2 * kBN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2 * D * VS];
   __shared__ int s_item;
 
   const int tid = threadIdx.x;
@@ -93,6 +107,8 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
   // staging coordinates: 16-byte chunk of a row, and the first of KPT keys
   const int sc = tid % CPR;
   const int sk = (tid / CPR) * KPT;
+  // this lane's V^T operand row (col) and key-group bit, see the layout note
+  const int vlane = col * VS + (((lg ^ (col >> 4)) & 1) << 2);
 
   const int n_items = w.hdr[H_TILES] * a.hkv;
   const int64_t page_stride = int64_t(kBlock) * ROW_BYTES;
@@ -160,50 +176,53 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
         gv[i] = in ? vp[i * (ROW_BYTES / 16)] : u32x4{0u, 0u, 0u, 0u};
       }
     };
+    // K row-major; V transposed: for each of the chunk's 8 dims, KPT consecutive keys
+    auto store_tile = [&](int buf) {
+      uint16_t* sk_base = s_k + buf * (kBN * KS);
+      uint16_t* sv_base = s_vt + buf * (D * VS);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) *reinterpret_cast<u32x4*>(&sk_base[(sk + i) * KS + sc * 8]) = gk[i];
+      uint32_t wv[KPT][4];
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        wv[i][0] = gv[i].x; wv[i][1] = gv[i].y; wv[i][2] = gv[i].z; wv[i][3] = gv[i].w;
+      }
+      // rows d = sc*8 + e share d>>4 = sc>>1, so one XOR per thread
+      uint16_t* vdst = sv_base + sc * 8 * VS + (((sk >> 2) ^ (sc >> 1)) << 2) + (sk & 3);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int dw = e >> 1;
+        const bool hi = e & 1;
+        uint16_t* dst = vdst + e * VS;
+        const uint32_t a0 = hi ? (wv[0][dw] >> 16) | (wv[1][dw] & 0xFFFF0000u)
+                               : (wv[0][dw] & 0xFFFFu) | (wv[1][dw] << 16);
+        if constexpr (KPT == 4) {
+          const uint32_t a1 = hi ? (wv[2][dw] >> 16) | (wv[3][dw] & 0xFFFF0000u)
+                                 : (wv[2][dw] & 0xFFFFu) | (wv[3][dw] << 16);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(a0, a1);
+        } else {
+          *reinterpret_cast<uint32_t*>(dst) = a0;
+        }
+      }
+    };
 
+    // prologue: tile 0 in LDS buffer 0, tile 1 in flight
     int32_t id_next = page_id(0);
     load_tile(0, id_next);
     if (n_kt > 1) id_next = page_id(1);
+    store_tile(0);
+    if (n_kt > 1) {
+      load_tile(1, id_next);
+      if (n_kt > 2) id_next = page_id(2);
+    }
+    __syncthreads();
 
-    for (int kt = 0; kt < n_kt; ++kt) {
-      __syncthreads();  // the previous tile's LDS reads are done
-      // K row-major
-#pragma unroll
-      for (int i = 0; i < KPT; ++i)
-        *reinterpret_cast<u32x4*>(&s_k[(sk + i) * KS + sc * 8]) = gk[i];
-      // V transposed: for each of the 8 dims of the chunk, KPT consecutive keys
-      {
-        uint32_t wv[KPT][4];
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-          wv[i][0] = gv[i].x; wv[i][1] = gv[i].y; wv[i][2] = gv[i].z; wv[i][3] = gv[i].w;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int dw = e >> 1;
-          const bool hi = e & 1;
-          uint16_t* dst = &s_vt[(sc * 8 + e) * VS + sk];
-          if constexpr (KPT == 4) {
-            const uint32_t a0 = hi ? (wv[0][dw] >> 16) | (wv[1][dw] & 0xFFFF0000u)
-                                   : (wv[0][dw] & 0xFFFFu) | (wv[1][dw] << 16);
-            const uint32_t a1 = hi ? (wv[2][dw] >> 16) | (wv[3][dw] & 0xFFFF0000u)
-                                   : (wv[2][dw] & 0xFFFFu) | (wv[3][dw] << 16);
-            *reinterpret_cast<uint2*>(dst) = make_uint2(a0, a1);
-          } else {
-            const uint32_t a0 = hi ? (wv[0][dw] >> 16) | (wv[1][dw] & 0xFFFF0000u)
-                                   : (wv[0][dw] & 0xFFFFu) | (wv[1][dw] << 16);
-            *reinterpret_cast<uint32_t*>(dst) = a0;
-          }
-        }
-      }
-      __syncthreads();  // tile kt is in LDS
-
-      // next tile's loads fly while this one is multiplied
-      if (kt + 1 < n_kt) {
-        load_tile(kt + 1, id_next);
-        if (kt + 2 < n_kt) id_next = page_id(kt + 2);
-      }
-
+    // tiles below n_full are visible to every row of the tile: no mask
+    const int n_full = (ctx + t0 + 1) / kBN;
+    auto tile_step = [&](int kt, auto masked) {
+      const int buf = kt & 1;
+      const uint16_t* ks = s_k + buf * (kBN * KS);
+      const uint16_t* vs = s_vt + buf * (D * VS);
       const int key0 = kt * kBN;
       // S^T = K Q^T: two 32-key blocks
       f32x16_t s[2];
@@ -212,36 +231,39 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
         s[mb] = f32x16_t{};
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(&s_k[(mb * 32 + col) * KS + kk * 16 + lg * 8]);
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(&ks[(mb * 32 + col) * KS + kk * 16 + lg * 8]);
           s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[kk]), s[mb], 0, 0, 0);
         }
       }
-      // causal mask (also hides keys past the tile's end): key > pos -> -inf
-      if (key0 + kBN - 1 > ctx + t0) {
+      // causal mask (also hides keys past the tile's end): key > pos -> -inf;
+      // accumulator row j of block mb is key key0 + lg*4 + mb*32 + (j/4)*8 + j%4
+      if constexpr (decltype(masked)::value) {
+        const int lim = pos - key0 - lg * 4;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = key0 + mb * 32 + (j / 4) * 8 + lg * 4 + (j % 4);
-            if (key > pos) s[mb][j] = -INFINITY;
-          }
+          for (int j = 0; j < 16; ++j)
+            if (mb * 32 + (j / 4) * 8 + (j % 4) > lim) s[mb][j] = -INFINITY;
       }
-      // online softmax for this lane's row (scores scaled into the log2 domain)
-      float mx = s[0][0];
+      // online softmax for this lane's row in the log2 domain.  The reference
+      // maximum m only moves when a row's maximum exceeds it by more than 2^8
+      // (lazy rescale): weights stay <= 2^8, exact in fp32 and bf16 range, and
+      // the final division by l cancels the common factor.
+      float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[0][j]);
+      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, fmaxf(s[0][j], s[1][j]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+      if (mx > m + 8.f) {
+        const float alpha = fast_exp2(m - mx);  // 0 on the first tile (m = -inf)
+        m = mx;
+        l *= alpha;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[1][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx * a.scale_log2);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      m = m_new;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
+        for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
+      }
+      const float m_use = m == -INFINITY ? 0.f : m;
 
-      // P^T in bf16 pairs: pk[mb][i] holds keys j = 2i, 2i+1 of block mb
+      // P^T in bf16 pairs: pk[mb][i] holds accumulator rows 2i, 2i+1 of block mb;
+      // the row sum adds the rounded weights (dot with (1, 1))
       uint32_t pk[2][8];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -250,7 +272,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
           const float p0 = fast_exp2(fmaf(s[mb][2 * i], a.scale_log2, -m_use));
           const float p1 = fast_exp2(fmaf(s[mb][2 * i + 1], a.scale_log2, -m_use));
           pk[mb][i] = pack_bf16(p0, p1);
-          l += bf16lo(pk[mb][i]) + bf16hi(pk[mb][i]);
+          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[mb][i]), kOnes, l, false);
         }
 
       // O^T += V^T P^T: four 16-key steps; step t uses accumulator rows
@@ -261,14 +283,29 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
                           pk[t / 2][(t % 2) * 4 + 3]};
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
-          const uint16_t* vrow = &s_vt[(db * 32 + col) * VS + 16 * t + lg * 4];
-          const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8);
+          // row d = db*32 + col: group u = 4t + lg (+2) sits at u ^ (2db + col/16);
+          // the lane's bit (lg ^ col/16) is in vlane, the rest is a constant
+          const uint16_t* vr = vs + vlane + db * 32 * VS;
+          const uint2 v0 = *reinterpret_cast<const uint2*>(vr + (((4 * t) ^ (2 * db)) << 2));
+          const uint2 v1 = *reinterpret_cast<const uint2*>(vr + (((4 * t + 2) ^ (2 * db)) << 2));
           const u32x4 va = {v0.x, v0.y, v1.x, v1.y};
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb), o[db], 0, 0, 0);
         }
       }
-    }
+
+      // stage tile kt+1 into the other buffer (its loads were issued a tile ago)
+      // and start the loads of tile kt+2; one barrier per tile
+      if (kt + 1 < n_kt) {
+        store_tile(buf ^ 1);
+        if (kt + 2 < n_kt) {
+          load_tile(kt + 2, id_next);
+          if (kt + 3 < n_kt) id_next = page_id(kt + 3);
+        }
+      }
+      __syncthreads();
+    };
+    for (int kt = 0; kt < min(n_full, n_kt); ++kt) tile_step(kt, std::false_type{});
+    for (int kt = max(n_full, 0); kt < n_kt; ++kt) tile_step(kt, std::true_type{});
 
     // the two lane halves hold disjoint keys of the same row
     l += __shfl_xor(l, 32);

@@ -46,7 +46,9 @@ struct Workspace {
   int32_t* hdr;        // [H_WORDS]
   int4* rows;          // [rows_cap]   {token row, seq, keys seen, 0}
   int64_t* rows_base;  // [rows_cap]   first unit of each row
-  int2* tiles;         // [tiles_cap]  {seq, first query row of the tile within the sequence}
+  int2* tiles;         // [tiles_cap]  {seq, first query row of the tile within the sequence},
+                       //   longest first
+  int4* tiles_tmp;     // [tiles_cap]  plan scratch: tiles in sequence order with their bucket
   int32_t* range_row;  // [ranges_cap] row holding each range's first unit
   int2* range_cut;     // [ranges_cap] {row, kv head} first cut by this range's start, or {-1, -1}
   float* part_o;       // [2 * ranges_cap * G * D] unnormalised partial outputs

@@ -13,8 +13,9 @@
 //
 // One workgroup of 1024 threads.  Pass 1 walks the sequences in chunks of
 // 1024 with block scans that place every tile record, row record and row's
-// first unit; pass 2 walks the rows and marks, for every range, the row
-// holding its first unit and the (row, kv head) it cuts.  It also clears the
+// first unit; the tiles are then sorted longest first; pass 2 walks the rows
+// and marks, for every range, the row holding its first unit and the (row, kv
+// head) it cuts.  It also clears the
 // work counter the chunk kernel uses.
 #include "internal.h"
 
@@ -22,6 +23,8 @@ namespace pa {
 namespace {
 
 constexpr int kWavesPerPlan = kPlanThreads / kWave;
+constexpr int kSortBuckets = kPlanThreads;  // key-count buckets of the tile sort, one per thread
+constexpr int kSortBucketKeys = 64;         // keys per bucket (one chunk-kernel key tile)
 
 // Exclusive scans of two non-negative int64 at once (one set of barriers).
 __device__ void block_exclusive_scan2(int64_t x, int64_t y, int64_t* ox, int64_t* oy, int64_t* tx, int64_t* ty,
@@ -91,6 +94,7 @@ __device__ __forceinline__ SeqInfo seq_info(const PlanArgs& a, int i) {
 __global__ void __launch_bounds__(kPlanThreads)
 plan_kernel(PlanArgs a, Workspace w) {
   __shared__ int64_t sh[2 * kWavesPerPlan];
+  __shared__ int s_hist[kSortBuckets];
   const int tid = threadIdx.x;
   const int64_t hkv = a.num_kv_heads;
 
@@ -110,9 +114,13 @@ plan_kernel(PlanArgs a, Workspace w) {
     int64_t off_tr, off_u, tot_tr, tot_u;
     block_exclusive_scan2((ntile << 32) | nrow, nunit, &off_tr, &off_u, &tot_tr, &tot_u, sh);
     const int64_t t0 = tiles + (off_tr >> 32), r0 = rows + (off_tr & 0xFFFFFFFFll);
-    // longest tiles of a sequence first: they see the most keys
-    for (int64_t t = 0; t < ntile && t0 + t < w.tiles_cap; ++t)
-      w.tiles[t0 + t] = make_int2(i, int32_t(ntile - 1 - t) * a.tile_rows);
+    // tile records with their key count (bucketed in kSortBucketKeys) for the sort below
+    for (int64_t t = 0; t < ntile && t0 + t < w.tiles_cap; ++t) {
+      const int32_t first = int32_t(t) * a.tile_rows;
+      const int32_t nt = min(a.tile_rows, s.q - first);
+      const int64_t bucket = (int64_t(s.c) + first + nt) / kSortBucketKeys;
+      w.tiles_tmp[t0 + t] = make_int4(i, first, int32_t(bucket < kSortBuckets ? bucket : kSortBuckets - 1), 0);
+    }
     int64_t u = units + off_u;
     for (int32_t j = 0; j < nrow && r0 + j < w.rows_cap; ++j) {
       const int32_t len = s.c + j + 1;
@@ -126,6 +134,28 @@ plan_kernel(PlanArgs a, Workspace w) {
   }
   if (tiles > w.tiles_cap) tiles = w.tiles_cap;  // only with inconsistent metadata
   if (rows > w.rows_cap) rows = w.rows_cap;
+  __syncthreads();  // tile records written above are read by other threads below
+
+  // chunk tiles longest first (counting sort on key count, descending), so
+  // the tiles that see the most keys start first and the tail stays short;
+  // the order inside a bucket does not matter
+  {
+    int* hist = s_hist;
+    hist[tid] = 0;  // one bucket per thread
+    __syncthreads();
+    for (int64_t t = tid; t < tiles; t += kPlanThreads)
+      atomicAdd(&hist[kSortBuckets - 1 - w.tiles_tmp[t].z], 1);
+    __syncthreads();
+    int64_t off, dummy, tot, tot2;
+    block_exclusive_scan2(hist[tid], 0, &off, &dummy, &tot, &tot2, sh);
+    hist[tid] = int(off);
+    __syncthreads();
+    for (int64_t t = tid; t < tiles; t += kPlanThreads) {
+      const int4 rec = w.tiles_tmp[t];
+      const int at = atomicAdd(&hist[kSortBuckets - 1 - rec.z], 1);
+      w.tiles[at] = make_int2(rec.x, rec.y);
+    }
+  }
 
   // the unit stream is cut into ranges of `per` units
   int64_t per = a.fixed_units > 0 ? a.fixed_units : (units + a.num_ranges - 1) / a.num_ranges;
