@@ -20,24 +20,31 @@
 // 16 rows (keys), so a query row's max and sum need only one exchange between
 // lanes l and l^32, and the bf16 weights P feed the PV product straight from
 // the S^T accumulator: the PV operand slots are matched to the keys the lane
-// holds, and V^T is read from LDS in the same key order.
+// holds, and V^T is read in the same key order.
+//
+// Staging is DMA: wavefront w copies page w of the tile (16 rows of K and of
+// V) from the pool into LDS with global_load_lds_dwordx4 (one wave-uniform
+// block id, each instruction fills 1 KiB of LDS in lane order), so K and V
+// never pass through registers.  K is read back as the MFMA A operand with
+// ds_read_b128; V stays row-major and ds_read_b64_tr_b16 returns it
+// transposed: within 16 lanes, lane i receives the (i%4)-th element of the 8
+// bytes addressed by lane 4k + i/4 for k = 0..3, so if lane s addresses
+// V[key0 + s/4][d0 + 4*(s%4)], lane i gets V[key0 + 0..3][d0 + i], a V^T
+// operand quarter.  Both tiles are XOR-swizzled by 16-byte chunk (K by the row
+// within its page, V by a table over row % 4) so the operand loads touch
+// distinct banks; the DMA chooses, per lane, the global chunk that belongs in
+// its LDS slot.  LDS holds two tiles: the DMA of tile kt+1 is issued before
+// tile kt is multiplied, and one barrier per tile closes both.
 //
 // Online softmax in the log2 domain on the VALU; P is rounded to bf16 for the
 // PV product and the row sum l adds the rounded values, so the output is an
-// exact convex combination of V rows with the rounded weights.  Keys past a
-// row's position get -inf by select; K and V of keys past the tile's last
-// position are written to LDS as zeros and never read from the pool, so
-// nothing outside the sequence reaches the products (NaN-safe).
-//
-// Staging: 256 threads load one 64-key tile of K and V (16 bytes per load, a
-// fully used 256-byte row segment per 16 lanes); K goes to LDS row-major, V is
-// transposed in registers (4 keys x 8 dims per thread) and written as V^T
-// (bank-conflict-free layout, see the V^T layout note).  LDS holds two tiles: while tile
-// kt is multiplied, tile kt+1 (loaded during tile kt-1) is staged into the
-// other buffer and the loads of tile kt+2 are issued, with one barrier per
-// tile.  The reference maximum of the online softmax moves lazily, so the O
-// accumulators are rescaled only when a row's maximum grows by more than 2^8.
-// Tiles are taken from a work counter, longest first within a sequence.
+// exact convex combination of V rows with the rounded weights.  The reference
+// maximum moves lazily (the O accumulators are rescaled only when a row's
+// maximum grows by more than 2^8).  Keys past a row's position get -inf by
+// select; V rows of keys past the tile's last position are zeroed in LDS after
+// the DMA (pages past the sequence are not read at all), so nothing outside
+// the sequence reaches the PV product (NaN-safe).  Tiles are taken from a
+// work counter, longest first.
 #include <type_traits>
 
 #include "internal.h"
@@ -49,6 +56,12 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+using I0 = std::integral_constant<int, 0>;
+using I1 = std::integral_constant<int, 1>;
 
 constexpr int kTileRows = 128;  // query rows per workgroup tile
 constexpr int kBN = 64;         // keys per K/V tile
@@ -64,54 +77,65 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// LDS layout of V^T[d][key]: rows are VS elements apart and the 8-byte key
-// groups of row d (four keys each) are permuted by XOR with d/16, i.e. group
-// u of row d sits at element d*VS + 4*(u ^ (d>>4)).  With VS = 68 both the
-// staging stores (16 lanes: rows 8 apart, one key group) and the operand loads
-// (16 lanes: consecutive rows, one key group) touch 32 distinct banks.
-
 constexpr bf16x2_t kOnes = {__bf16(1.0f), __bf16(1.0f)};
+
+// XOR swizzle of V's 16-byte chunks by row % 4 (a table found to make the
+// transposed operand loads touch distinct banks in 16- and 32-lane groups)
+__device__ __forceinline__ int v_swz(int row) { return (0xEA40 >> ((row & 3) * 4)) & 15; }  // {0, 4, 10, 14}
 
 template <int D>
 struct ChunkCfg {
-  static constexpr int KSTEPS = D / 16;            // MFMA k-steps of Q.K (16 dims each)
-  static constexpr int DBLK = D / 32;              // 32-dim blocks of O^T
-  static constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
-  static constexpr int KPT = kBN * CPR / kThreads; // keys staged per thread: 4 (D=128) or 2 (D=64)
-  static constexpr int KS = D + 8;                 // LDS row stride of K (elements), padded
-  static constexpr int VS = kBN + 4;               // LDS row stride of V^T (elements), padded
-  static_assert(KPT == 2 || KPT == 4, "staging layout");
+  static constexpr int RB = D * 2;                  // bytes per K/V row
+  static constexpr int CH = RB / 16;                // 16-byte chunks per row: 16 or 8
+  static constexpr int RPI = kWave / CH;            // rows per DMA instruction: 4 or 8
+  static constexpr int IPG = kBlock / RPI;          // DMA instructions per page and tensor
+  static constexpr int KSTEPS = D / 16;             // MFMA k-steps of Q.K (16 dims each)
+  static constexpr int DBLK = D / 32;               // 32-dim blocks of O^T
+  static constexpr int TILE_BYTES = kBN * RB;       // one K or V tile
 };
 
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads, 2)
 chunk_mfma_kernel(AttnArgs a, Workspace w) {
   using C = ChunkCfg<D>;
-  constexpr int KSTEPS = C::KSTEPS, DBLK = C::DBLK, CPR = C::CPR, KPT = C::KPT, KS = C::KS, VS = C::VS;
+  constexpr int RB = C::RB, CH = C::CH, RPI = C::RPI, IPG = C::IPG, KSTEPS = C::KSTEPS, DBLK = C::DBLK;
   constexpr int TQ = kTileRows / G;  // tokens per tile
-  constexpr int ROW_BYTES = D * 2;
 
-  // two buffers each: the next tile is staged while this one is multiplied
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2 * kBN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2 * D * VS];
+  // two buffers of each: tile kt+1 lands while tile kt is multiplied.  Four
+  // separate arrays, each step naming its buffers at compile time, so the
+  // compiler can see that the DMA in flight does not write what is being read
+  // (it would otherwise wait for the DMA before every LDS read)
+  __shared__ __attribute__((aligned(16))) char s_k0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char s_k1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char s_v0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char s_v1[C::TILE_BYTES];
   __shared__ int s_item;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int col = lane & 31;  // accumulator column = query row within the wavefront
   const int lg = lane >> 5;   // lane half
-  // staging coordinates: 16-byte chunk of a row, and the first of KPT keys
-  const int sc = tid % CPR;
-  const int sk = (tid / CPR) * KPT;
-  // this lane's V^T operand row (col) and key-group bit, see the layout note
-  const int vlane = col * VS + (((lg ^ (col >> 4)) & 1) << 2);
+
+  // K operand (ds_read_b128): row mb*32 + col, chunk (2kk + lg) ^ (col % CH) = 2kk ^ kx
+  const int kx = lg ^ (col & (CH - 1));
+  // V operand (ds_read_b64_tr_b16): source lane s addresses row 4*lg + s/4 (+ 16t + 8e)
+  // and dims 32db + 16*(col/16) + 4*(s%4) (chunk c, half s&1), swizzled by row % 4 = s/4
+  int vaddr[DBLK];
+  {
+    const int s = lane & 15, q = s >> 2, h16 = col >> 4;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const int c = 4 * db + 2 * h16 + ((s >> 1) & 1);
+      vaddr[db] = (4 * lg + q) * RB + 16 * ((c ^ v_swz(q)) & (CH - 1)) + 8 * (s & 1);
+    }
+  }
+  // DMA: in instruction j of a page, lane -> row j*RPI + lane/CH of the page,
+  // LDS chunk lane%CH, which holds global chunk (lane%CH) ^ swizzle(row)
+  const int dma_row = lane / CH, dma_chunk = lane % CH;
 
   const int n_items = w.hdr[H_TILES] * a.hkv;
-  const int64_t page_stride = int64_t(kBlock) * ROW_BYTES;
+  const int64_t page_stride = int64_t(kBlock) * RB;
   const char* kbase = static_cast<const char*>(a.kc);
   const char* vbase = static_cast<const char*>(a.vc);
 
@@ -132,7 +156,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
     // outside q, out or the block-table row even with inconsistent metadata
     const int qlen = min(min(a.qsl[seq + 1] - r0, a.num_tokens - r0), a.mbps * kBlock - ctx);
     const int nt = max(0, min(TQ, qlen - t0));  // valid tokens of this tile
-    const int kv_end = ctx + t0 + nt;   // keys seen by the tile's last row
+    const int kv_end = ctx + t0 + nt;           // keys seen by the tile's last row
     const int n_kt = (kv_end + kBN - 1) / kBN;
     const int n_pages = (kv_end + kBlock - 1) / kBlock;
     const int32_t* btrow = a.bt + int64_t(seq) * a.mbps;
@@ -147,7 +171,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
     u32x4 qf[KSTEPS];
     {
       const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) +
-                                                       ((int64_t(r0) + t0 + tt) * a.hq + head) * ROW_BYTES);
+                                                       ((int64_t(r0) + t0 + tt) * a.hq + head) * RB);
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = valid ? qp[2 * kk + lg] : u32x4{0u, 0u, 0u, 0u};
     }
@@ -157,82 +181,77 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
     for (int db = 0; db < DBLK; ++db) o[db] = f32x16_t{};
     float m = -INFINITY, l = 0.f;
 
-    // staging registers: KPT keys x one 16-byte chunk of K and of V
-    u32x4 gk[KPT], gv[KPT];
+    // block id of this wavefront's page in tile kt (raw: made wave-uniform and
+    // clamped where it is used, a tile later, so its load is not waited for here
+    // -- vector loads retire in order, so that wait would also wait for the DMA)
     auto page_id = [&](int kt) -> int32_t {
-      const int page = (kt * kBN + sk) / kBlock;
-      int32_t b = page < n_pages ? btrow[page] : 0;
-      return b < 0 ? 0 : (b >= a.nb ? int32_t(a.nb - 1) : b);
+      const int page = kt * 4 + wave;
+      return page < n_pages ? btrow[page] : 0;
     };
-    auto load_tile = [&](int kt, int32_t blk) {
-      const int key = kt * kBN + sk;
-      const int64_t off = (int64_t(blk) * a.hkv + kvh) * page_stride + int64_t(key % kBlock) * ROW_BYTES + sc * 16;
-      const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + off);
-      const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + off);
+    // DMA of this wavefront's page of tile kt into buffer buf (nothing past the sequence)
+    auto dma_tile = [&](int kt, auto bufc, int32_t raw) {
+      constexpr int buf = decltype(bufc)::value;
+      char* dk = buf ? s_k1 : s_k0;
+      char* dv = buf ? s_v1 : s_v0;
+      if (kt * 4 + wave >= n_pages) return;
+      raw = __builtin_amdgcn_readfirstlane(raw);
+      const int32_t blk = raw < 0 ? 0 : (raw >= a.nb ? int32_t(a.nb - 1) : raw);  // never leave the pool
+      const int64_t page = (int64_t(blk) * a.hkv + kvh) * page_stride;
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const bool in = key + i < kv_end;
-        gk[i] = in ? kp[i * (ROW_BYTES / 16)] : u32x4{0u, 0u, 0u, 0u};
-        gv[i] = in ? vp[i * (ROW_BYTES / 16)] : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < IPG; ++j) {
+        const int row = j * RPI + dma_row;  // token within the page
+        const int64_t g_k = page + int64_t(row) * RB + 16 * (dma_chunk ^ (row & (CH - 1)));
+        const int64_t g_v = page + int64_t(row) * RB + 16 * (dma_chunk ^ (v_swz(row) & (CH - 1)));
+        const int lrow = wave * kBlock + j * RPI;  // first LDS row of this instruction
+        __builtin_amdgcn_global_load_lds(kbase + g_k, (lds_void_t*)(dk + lrow * RB), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vbase + g_v, (lds_void_t*)(dv + lrow * RB), 16, 0, 0);
       }
     };
-    // K row-major; V transposed: for each of the chunk's 8 dims, KPT consecutive keys
-    auto store_tile = [&](int buf) {
-      uint16_t* sk_base = s_k + buf * (kBN * KS);
-      uint16_t* sv_base = s_vt + buf * (D * VS);
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) *reinterpret_cast<u32x4*>(&sk_base[(sk + i) * KS + sc * 8]) = gk[i];
-      uint32_t wv[KPT][4];
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        wv[i][0] = gv[i].x; wv[i][1] = gv[i].y; wv[i][2] = gv[i].z; wv[i][3] = gv[i].w;
-      }
-      // rows d = sc*8 + e share d>>4 = sc>>1, so one XOR per thread
-      uint16_t* vdst = sv_base + sc * 8 * VS + (((sk >> 2) ^ (sc >> 1)) << 2) + (sk & 3);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dw = e >> 1;
-        const bool hi = e & 1;
-        uint16_t* dst = vdst + e * VS;
-        const uint32_t a0 = hi ? (wv[0][dw] >> 16) | (wv[1][dw] & 0xFFFF0000u)
-                               : (wv[0][dw] & 0xFFFFu) | (wv[1][dw] << 16);
-        if constexpr (KPT == 4) {
-          const uint32_t a1 = hi ? (wv[2][dw] >> 16) | (wv[3][dw] & 0xFFFF0000u)
-                                 : (wv[2][dw] & 0xFFFFu) | (wv[3][dw] << 16);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(a0, a1);
-        } else {
-          *reinterpret_cast<uint32_t*>(dst) = a0;
-        }
+    // after the DMA has landed: V rows of keys at or past kv_end become zeros
+    auto zero_tail = [&](int kt, auto bufc) {
+      char* dv = decltype(bufc)::value ? s_v1 : s_v0;
+      const int key0 = kt * kBN + wave * kBlock;  // first key of this wavefront's page
+      if (key0 + kBlock <= kv_end) return;
+      for (int idx = lane; idx < kBlock * CH; idx += kWave) {
+        const int row = idx / CH;
+        if (key0 + row >= kv_end)
+          *reinterpret_cast<u32x4*>(dv + (wave * kBlock + row) * RB + (idx % CH) * 16) = u32x4{0u, 0u, 0u, 0u};
       }
     };
 
-    // prologue: tile 0 in LDS buffer 0, tile 1 in flight
+    // prologue: tile 0 in buffer 0
     int32_t id_next = page_id(0);
-    load_tile(0, id_next);
+    dma_tile(0, I0{}, id_next);
     if (n_kt > 1) id_next = page_id(1);
-    store_tile(0);
-    if (n_kt > 1) {
-      load_tile(1, id_next);
-      if (n_kt > 2) id_next = page_id(2);
-    }
+    __builtin_amdgcn_s_waitcnt(0);
+    zero_tail(0, I0{});
     __syncthreads();
 
     // tiles below n_full are visible to every row of the tile: no mask
     const int n_full = (ctx + t0 + 1) / kBN;
-    auto tile_step = [&](int kt, auto masked) {
-      const int buf = kt & 1;
-      const uint16_t* ks = s_k + buf * (kBN * KS);
-      const uint16_t* vs = s_vt + buf * (D * VS);
+    auto tile_step = [&](int kt, auto bufc, auto masked) {
+      constexpr int buf = decltype(bufc)::value;
+      using Other = std::integral_constant<int, buf ^ 1>;
+      // the next tile's DMA flies while this one is multiplied
+      if (kt + 1 < n_kt) {
+        dma_tile(kt + 1, Other{}, id_next);
+        if (kt + 2 < n_kt) id_next = page_id(kt + 2);
+      }
+      const char* ks = buf ? s_k1 : s_k0;
+      const char* vs = buf ? s_v1 : s_v0;
       const int key0 = kt * kBN;
-      // S^T = K Q^T: two 32-key blocks
-      f32x16_t s[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        s[mb] = f32x16_t{};
+
+      // S^T = K Q^T: two 32-key blocks, the chains interleaved
+      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+      {
+        const char* kr = ks + col * RB;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(&ks[(mb * 32 + col) * KS + kk * 16 + lg * 8]);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[kk]), s[mb], 0, 0, 0);
+          const int off = 16 * ((2 * kk) ^ kx);
+          const u32x4 k0 = *reinterpret_cast<const u32x4*>(kr + off);
+          const u32x4 k1 = *reinterpret_cast<const u32x4*>(kr + 32 * RB + off);
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), as_bf16x8(qf[kk]), s[0], 0, 0, 0);
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), as_bf16x8(qf[kk]), s[1], 0, 0, 0);
         }
       }
       // causal mask (also hides keys past the tile's end): key > pos -> -inf;
@@ -276,36 +295,42 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
         }
 
       // O^T += V^T P^T: four 16-key steps; step t uses accumulator rows
-      // j = (t%2)*8 .. +8 of block t/2, i.e. keys 16t + (i/4)*8 + lg*4 + i%4
+      // j = (t%2)*8 .. +8 of block t/2, i.e. keys 16t + (i/4)*8 + lg*4 + i%4,
+      // loaded as two transposed quarters (i = 0..3: rows 16t + 4lg + k,
+      // i = 4..7: rows 16t + 8 + 4lg + k)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const u32x4 pb = {pk[t / 2][(t % 2) * 4 + 0], pk[t / 2][(t % 2) * 4 + 1], pk[t / 2][(t % 2) * 4 + 2],
                           pk[t / 2][(t % 2) * 4 + 3]};
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
-          // row d = db*32 + col: group u = 4t + lg (+2) sits at u ^ (2db + col/16);
-          // the lane's bit (lg ^ col/16) is in vlane, the rest is a constant
-          const uint16_t* vr = vs + vlane + db * 32 * VS;
-          const uint2 v0 = *reinterpret_cast<const uint2*>(vr + (((4 * t) ^ (2 * db)) << 2));
-          const uint2 v1 = *reinterpret_cast<const uint2*>(vr + (((4 * t + 2) ^ (2 * db)) << 2));
-          const u32x4 va = {v0.x, v0.y, v1.x, v1.y};
+          const char* vr = vs + vaddr[db] + 16 * t * RB;
+          const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vr));
+          const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vr + 8 * RB));
+          const u32x4 va = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1)),
+                            __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3)),
+                            __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1)),
+                            __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3))};
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb), o[db], 0, 0, 0);
         }
       }
 
-      // stage tile kt+1 into the other buffer (its loads were issued a tile ago)
-      // and start the loads of tile kt+2; one barrier per tile
+      // tile kt+1 has landed (and its tail is zeroed) before anyone reads it;
+      // everyone is done with buffer buf before the DMA of tile kt+2 reuses it
       if (kt + 1 < n_kt) {
-        store_tile(buf ^ 1);
-        if (kt + 2 < n_kt) {
-          load_tile(kt + 2, id_next);
-          if (kt + 3 < n_kt) id_next = page_id(kt + 3);
-        }
+        __builtin_amdgcn_s_waitcnt(0);
+        zero_tail(kt + 1, Other{});
       }
       __syncthreads();
     };
-    for (int kt = 0; kt < min(n_full, n_kt); ++kt) tile_step(kt, std::false_type{});
-    for (int kt = max(n_full, 0); kt < n_kt; ++kt) tile_step(kt, std::true_type{});
+    auto step = [&](int kt, auto masked) {
+      if (kt & 1)
+        tile_step(kt, I1{}, masked);
+      else
+        tile_step(kt, I0{}, masked);
+    };
+    for (int kt = 0; kt < min(n_full, n_kt); ++kt) step(kt, std::false_type{});
+    for (int kt = max(n_full, 0); kt < n_kt; ++kt) step(kt, std::true_type{});
 
     // the two lane halves hold disjoint keys of the same row
     l += __shfl_xor(l, 32);

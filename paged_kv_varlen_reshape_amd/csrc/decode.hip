@@ -395,8 +395,11 @@ hipError_t launch_decode_t(const AttnArgs& a, const Workspace& w, hipStream_t st
 
 template <int D, int G>
 hipError_t launch_merge_t(const AttnArgs& a, const Workspace& w, hipStream_t st) {
+  // one wavefront per (range, head) job would be ranges*G wavefronts, almost
+  // all idle (only cut pairs have work): a few workgroups per CU loop instead
   int64_t grid = (w.ranges_cap * G + 3) / 4;
-  if (grid > 8192) grid = 8192;
+  const int64_t cap = int64_t(device_cus()) * 2;
+  if (grid > cap) grid = cap;
   hipLaunchKernelGGL((split_merge_kernel<D, G>), dim3(unsigned(grid)), dim3(256), 0, st, a, w);
   return hipGetLastError();
 }

@@ -139,7 +139,7 @@ plan_kernel(PlanArgs a, Workspace w) {
   // chunk tiles longest first (counting sort on key count, descending), so
   // the tiles that see the most keys start first and the tail stays short;
   // the order inside a bucket does not matter
-  {
+  if (tiles > 0) {
     int* hist = s_hist;
     hist[tid] = 0;  // one bucket per thread
     __syncthreads();
