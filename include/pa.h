@@ -140,8 +140,11 @@ enum {
                                 pages spread evenly over the resident wavefronts */
   PA_OPT_TARGET_ITEMS = 3,   /* >0: number of decode ranges in automatic mode; 0: one per
                                 resident decode wavefront */
-  PA_OPT_DECODE_BUFFERS = 4  /* 1 or 2: pages in registers per decode wavefront (2 = the next
-                                page's loads overlap this page's math); 0: automatic */
+  PA_OPT_DECODE_BUFFERS = 4, /* 1 or 2: pages in registers per wavefront of the VALU row-wise
+                                kernel (2 = the next page's loads overlap this page's math);
+                                0: automatic */
+  PA_OPT_DECODE_KERNEL = 5   /* row-wise rows of bf16 steps: 0 automatic (MFMA), 1 VALU kernel,
+                                2 MFMA kernel; float32 steps always take the VALU kernel */
 };
 int pa_set_option(int32_t option, int64_t value);
 int64_t pa_get_option(int32_t option);

@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     PA_OPT_SPLIT_TOKENS,
     PA_OPT_TARGET_ITEMS,
     PA_OPT_DECODE_BUFFERS,
+    PA_OPT_DECODE_KERNEL,
     PA_K_CHUNK,
     PA_K_COUNT,
     PA_K_DECODE,

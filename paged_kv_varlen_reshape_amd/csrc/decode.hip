@@ -323,22 +323,23 @@ decode_streamk_kernel(AttnArgs a, Workspace w) {
 // first cuts the pair (r, k) recorded for it; the pair's pieces are the last
 // segment of the range holding its first unit (slot 0 if that range starts
 // exactly there, else slot 1) and the first segment (slot 0) of every later
-// range up to the one holding its last unit.  One wavefront per (cut, query
-// head of the group) folds the pieces with a running maximum:
+// range up to the one holding its last unit.  One wavefront per range folds
+// all G heads of its pair with a running maximum:
 //   M = max_s m_s;  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
-// Each lane owns D/64 consecutive elements, so every piece is one coalesced
-// load per wavefront.
+// Lane l owns E = G*D/64 consecutive elements of the pair's G x D output (one
+// head each), so every piece is read with wide coalesced loads.
 template <int D, int G>
 __global__ void __launch_bounds__(256)
 split_merge_kernel(AttnArgs a, Workspace w) {
-  constexpr int E = D / kWave;  // elements per lane: 1 or 2
+  constexpr int E = G * D / kWave;  // elements per lane: 1..16
+  constexpr int V4 = E >= 4 ? E / 4 : 0;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t n_jobs = int64_t(w.hdr[H_RANGES]) * G;
+  const int64_t nr = w.hdr[H_RANGES];
   const int64_t per = w.hdr64[H64_PER];
   const int64_t waves = int64_t(gridDim.x) * (blockDim.x / kWave);
-  for (int64_t job = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave; job < n_jobs; job += waves) {
-    const int64_t g = job / G;
-    const int h = int(job - g * G);
+  const int e0 = lane * E;
+  const int h = e0 / D;  // head of this lane's elements
+  for (int64_t g = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave; g < nr; g += waves) {
     const int2 cut = w.range_cut[g];
     if (g == 0 || cut.x < 0) continue;
     const int4 rec = w.rows[cut.x];
@@ -351,10 +352,18 @@ split_merge_kernel(AttnArgs a, Workspace w) {
     for (int64_t gg = g0; gg <= g1; ++gg) {
       const int64_t slot = gg * 2 + (gg == g0 && f != g0 * per ? 1 : 0);
       const float2 ml = w.part_ml[slot * G + h];
-      const float* po = w.part_o + (slot * G + h) * D + lane * E;
+      const float* po = w.part_o + slot * G * D + e0;
       float v[E];
+      if constexpr (V4 > 0) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) v[e] = po[e];
+        for (int c = 0; c < V4; ++c) {
+          const float4 t = reinterpret_cast<const float4*>(po)[c];
+          v[4 * c] = t.x; v[4 * c + 1] = t.y; v[4 * c + 2] = t.z; v[4 * c + 3] = t.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = po[e];
+      }
       const float Mn = fmaxf(M, ml.x);
       const float fo = fast_exp2(M - Mn), fn = fast_exp2(ml.x - Mn);
       lsum = lsum * fo + ml.y * fn;
@@ -362,9 +371,17 @@ split_merge_kernel(AttnArgs a, Workspace w) {
       for (int e = 0; e < E; ++e) acc[e] = acc[e] * fo + v[e] * fn;
       M = Mn;
     }
-    float* op = a.out + (int64_t(rec.x) * a.hq + int64_t(cut.y) * G + h) * D + lane * E;
+    const float inv = 1.f / lsum;
+    float* op = a.out + (int64_t(rec.x) * a.hq + int64_t(cut.y) * G) * D + e0;
+    if constexpr (V4 > 0) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) op[e] = acc[e] / lsum;
+      for (int c = 0; c < V4; ++c)
+        reinterpret_cast<float4*>(op)[c] =
+            make_float4(acc[4 * c] * inv, acc[4 * c + 1] * inv, acc[4 * c + 2] * inv, acc[4 * c + 3] * inv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) op[e] = acc[e] * inv;
+    }
   }
 }
 
@@ -395,11 +412,9 @@ hipError_t launch_decode_t(const AttnArgs& a, const Workspace& w, hipStream_t st
 
 template <int D, int G>
 hipError_t launch_merge_t(const AttnArgs& a, const Workspace& w, hipStream_t st) {
-  // one wavefront per (range, head) job would be ranges*G wavefronts, almost
-  // all idle (only cut pairs have work): a few workgroups per CU loop instead
-  int64_t grid = (w.ranges_cap * G + 3) / 4;
-  const int64_t cap = int64_t(device_cus()) * 2;
-  if (grid > cap) grid = cap;
+  // one wavefront per range: each merge is a short chain of dependent loads,
+  // so they all run side by side (a range without a cut exits at once)
+  const int64_t grid = (w.ranges_cap + 3) / 4;
   hipLaunchKernelGGL((split_merge_kernel<D, G>), dim3(unsigned(grid)), dim3(256), 0, st, a, w);
   return hipGetLastError();
 }
@@ -455,13 +470,20 @@ int decode_buffers(int group) {
   return group >= 8 ? 1 : 2;
 }
 
+bool decode_uses_mfma(int bf16) {
+  const int64_t v = option(PA_OPT_DECODE_KERNEL);
+  return bf16 && v != 1;
+}
+
 int decode_waves(int bf16, int head_dim, int group) {
+  if (decode_uses_mfma(bf16)) return decode_mfma_waves(head_dim, group);
   const int nbuf = decode_buffers(group);
   if (bf16) return head_dim == 64 ? waves_d<true, 64>(group, nbuf) : waves_d<true, 128>(group, nbuf);
   return head_dim == 64 ? waves_d<false, 64>(group, nbuf) : waves_d<false, 128>(group, nbuf);
 }
 
 hipError_t launch_decode(const AttnArgs& a, const Workspace& w, int group, hipStream_t st) {
+  if (decode_uses_mfma(a.bf16)) return launch_decode_mfma(a, w, group, st);
   const int nbuf = decode_buffers(group);
   if (a.bf16)
     return a.d == 64 ? launch_decode_d<true, 64>(a, w, group, nbuf, st) : launch_decode_d<true, 128>(a, w, group, nbuf, st);

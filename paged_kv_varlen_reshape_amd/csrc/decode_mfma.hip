@@ -1,0 +1,339 @@
+// decode_mfma: row-wise attention over the paged cache on bf16 MFMA.
+//
+// Same work as the row-wise VALU kernel (decode rows, and every row of a
+// chunk when the chunk kernel is off): a row at absolute position p sees keys
+// 0..p of its own sequence, read through 16-token blocks (Inside vLLM summary,
+// techfeed.io, section "PagedAttentionの仕組み"); decoding is bound by memory
+// bandwidth (section "エンジンの中核：スケジューラとKVキャッシュ管理").  The
+// work decomposition is the same stream-K walk: every resident wavefront
+// streams an equal range of (row, kv head, page) units, writing the
+// normalised output for whole (row, kv head) segments and (o, max, sum)
+// partials for segments a range boundary cuts (split_merge folds them).
+//
+// Per 16-token page of one kv head, with the GQA group's G query heads:
+//   S^T[key][head] = K Q^T  on v_mfma_f32_16x16x32_bf16 (A = K straight from
+//     the pool into registers: lane l holds key l%16, dims 8*(l/16) + 32kk;
+//     B = Q: lane l holds head l%16 -- zeros past G -- same dims);
+//   in the 16x16 accumulator lane l holds head l%16 and keys 4*(l/16) + 0..3,
+//   so a head's page maximum needs two cross-lane steps, and the bf16 weights
+//   are already the B operand of
+//   O^T[dim][head] += V^T P^T on v_mfma_f32_16x16x16_bf16 (A = V^T: each
+//     wavefront DMAs its V page into its own LDS buffer with
+//     global_load_lds_dwordx4 and reads it back transposed with
+//     ds_read_b64_tr_b16; within 16 lanes, lane i receives the (i%4)-th
+//     element of the 8 bytes lane 4k + i/4 addresses, so source lane s
+//     addresses V[4g + s/4][16dblk + 4*(s%4)] and lane i gets
+//     V[4g + 0..3][16dblk + i] for its lane group g).
+// The page's 16-byte chunks are XOR-swizzled by row (2*(row%4) + 8*(row/4%2))
+// so the transposed loads touch distinct banks; the DMA picks, per lane, the
+// global chunk that belongs in its LDS slot.  Two LDS page buffers per
+// wavefront (separate arrays, named at compile time) let the next page's K
+// loads and V DMA fly while the current page is multiplied, with no barrier.
+//
+// Softmax in fp32 in the log2 domain; P is rounded to bf16 for the PV product
+// and l sums the rounded weights, so each output is an exact convex
+// combination of V rows with the rounded weights.  The reference maximum
+// moves lazily (rescale only when a head's maximum grows by more than 2^8).
+// Keys past the row get -inf by select and their V rows are zeroed in LDS
+// after the DMA, so nothing outside the sequence reaches the products.
+#include <type_traits>
+
+#include "internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+using B0 = std::integral_constant<int, 0>;
+using B1 = std::integral_constant<int, 1>;
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2_t h = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+template <int D>
+struct DecM {
+  static constexpr int RB = D * 2;          // bytes per K/V row
+  static constexpr int CH = RB / 16;        // 16-byte chunks per row: 16 or 8
+  static constexpr int RPI = kWave / CH;    // rows per DMA instruction: 4 or 8
+  static constexpr int IPG = kBlock / RPI;  // DMA instructions per page
+  static constexpr int KS = D / 32;         // QK k-steps (32 dims each)
+  static constexpr int DB = D / 16;         // 16-dim blocks of O^T
+  static constexpr int PAGE = kBlock * RB;  // bytes of one (block, kv head) page
+};
+
+// chunk swizzle of V page row `row` (a bijection of the row's chunks)
+template <int CH>
+__device__ __forceinline__ int v_swz(int row) {
+  return (2 * (row & 3) + 8 * ((row >> 2) & 1)) & (CH - 1);
+}
+
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(N | (7 << 4) | (15 << 8));
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads, 3)
+decode_mfma_kernel(AttnArgs a, Workspace w) {
+  using C = DecM<D>;
+  constexpr int RB = C::RB, CH = C::CH, RPI = C::RPI, IPG = C::IPG, KS = C::KS, DB = C::DB, PAGE = C::PAGE;
+  static_assert(G <= 16, "one 16-wide accumulator column per head");
+
+  // two page buffers per wavefront, separate arrays so that the compiler sees
+  // the DMA in flight does not write what is being read
+  __shared__ __attribute__((aligned(16))) char s_v0[kWaves][PAGE];
+  __shared__ __attribute__((aligned(16))) char s_v1[kWaves][PAGE];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int gwave = blockIdx.x * kWaves + wave;
+  const int nwaves = gridDim.x * kWaves;
+  const int hq = lane & 15;   // accumulator column: query head within the group
+  const int grp = lane >> 4;  // lane group: keys 4grp..4grp+3 of a page in S
+  const bool head_ok = hq < G;
+
+  // V^T operand addresses of this lane (transposed reads, see the header)
+  int vaddr[DB];
+  {
+    const int s = lane & 15;
+    const int row = 4 * grp + (s >> 2);
+    const int F = v_swz<CH>(row);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vaddr[db] = row * RB + 16 * (((2 * db) + ((s >> 1) & 1)) ^ F) + 8 * (s & 1);
+  }
+  // DMA: in instruction j of a page, lane -> row j*RPI + lane/CH, LDS chunk lane%CH
+  const int dma_row = lane / CH, dma_chunk = lane % CH;
+
+  const int nranges = w.hdr[H_RANGES];
+  const int64_t units = w.hdr64[H64_UNITS];
+  const int64_t per = w.hdr64[H64_PER];
+  const char* kbase = static_cast<const char*>(a.kc);
+  const char* vbase = static_cast<const char*>(a.vc);
+
+  for (int g = gwave; g < nranges; g += nwaves) {
+    int64_t x = g * per;
+    const int64_t x_end = min(x + per, units);
+    int r = w.range_row[g];
+    int4 rec = w.rows[r];
+    int64_t base = w.rows_base[r];
+    int pages = (rec.z + kBlock - 1) / kBlock;
+    int kvh = int((x - base) / pages);
+    int p0 = int(x - base - int64_t(kvh) * pages);
+    bool first = true;
+
+    while (x < x_end) {
+      const int tok = rec.x, seq = rec.y, len = rec.z;
+      const int n = int(min(int64_t(pages - p0), x_end - x));  // pages of this segment
+      const int32_t* btrow = a.bt + int64_t(seq) * a.mbps + p0;
+
+      // Q as the B operand: head hq (zeros past G), dims 8*grp + 32kk
+      u32x4 qf[KS];
+      {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) +
+                                                         (int64_t(tok) * a.hq + int64_t(kvh) * G + hq) * RB);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) qf[kk] = head_ok ? qp[grp + 4 * kk] : u32x4{0u, 0u, 0u, 0u};
+      }
+
+      f32x4_t o[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = f32x4_t{};
+      float m = -INFINITY, l = 0.f;
+
+      // block ids of the segment's pages, 64 at a time: lane j holds page j of the batch
+      int32_t ids = 0;
+      auto load_ids = [&](int j0) {
+        const int j = j0 + lane;
+        const int32_t b = j < n ? btrow[j] : 0;
+        ids = b < 0 ? 0 : (b >= a.nb ? int32_t(a.nb - 1) : b);  // never leave the pool
+      };
+      auto page_base = [&](int j) -> int64_t {
+        const int32_t b = __builtin_amdgcn_readlane(ids, j & (kWave - 1));
+        return (int64_t(b) * a.hkv + kvh) * PAGE;
+      };
+      // K of page j straight into the A-operand layout; V of page j by DMA into buffer B
+      auto issue = [&](int j, u32x4 (&kf)[KS], auto bufc) {
+        if (j > 0 && (j & (kWave - 1)) == 0) load_ids(j);
+        const int64_t pb = page_base(j);
+        char* dv = (decltype(bufc)::value ? s_v1 : s_v0)[wave];
+#pragma unroll
+        for (int ii = 0; ii < IPG; ++ii) {
+          const int row = ii * RPI + dma_row;
+          const int64_t gv = pb + int64_t(row) * RB + 16 * (dma_chunk ^ v_swz<CH>(row));
+          __builtin_amdgcn_global_load_lds(vbase + gv, (lds_void_t*)(dv + ii * RPI * RB), 16, 0, 0);
+        }
+        const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + pb + int64_t(hq) * RB);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) kf[kk] = __builtin_nontemporal_load(kp + grp + 4 * kk);
+      };
+      // one page: scores, online softmax, PV
+      auto compute = [&](int j, const u32x4 (&kf)[KS], auto bufc) {
+        char* vs = (decltype(bufc)::value ? s_v1 : s_v0)[wave];
+        const int pos0 = (p0 + j) * kBlock;  // first key of the page
+        if (pos0 + kBlock > len) {
+          // last, partly filled page: its V rows past the row must not reach PV
+          for (int idx = lane; idx < kBlock * CH; idx += kWave)
+            if (pos0 + idx / CH >= len) *reinterpret_cast<u32x4*>(vs + idx * 16) = u32x4{0u, 0u, 0u, 0u};
+        }
+        f32x4_t s = f32x4_t{};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]),
+                                                     __builtin_bit_cast(bf16x8_t, qf[kk]), s, 0, 0, 0);
+        const int kfirst = pos0 + 4 * grp;  // key of accumulator row 0 of this lane
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = kfirst + i < len ? s[i] * a.scale_log2 : -INFINITY;
+        float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (mx > m + 8.f) {  // lazy rescale: weights stay <= 2^8
+          const float alpha = fast_exp2(m - mx);
+          m = mx;
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        }
+        const float m_use = m == -INFINITY ? 0.f : m;
+        const uint32_t p01 = pack_bf16(fast_exp2(s[0] - m_use), fast_exp2(s[1] - m_use));
+        const uint32_t p23 = pack_bf16(fast_exp2(s[2] - m_use), fast_exp2(s[3] - m_use));
+        l += __uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u) + __uint_as_float(p23 << 16) +
+             __uint_as_float(p23 & 0xFFFF0000u);
+        const bf16x4_t pb = __builtin_bit_cast(bf16x4_t, make_uint2(p01, p23));
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs + vaddr[db]));
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, v), pb, o[db], 0, 0, 0);
+        }
+      };
+
+      load_ids(0);
+      u32x4 ka[KS], kb[KS];
+      issue(0, ka, B0{});
+      for (int j = 0; j < n; j += 2) {
+        // page j+1 flies while page j is multiplied
+        if (j + 1 < n) {
+          issue(j + 1, kb, B1{});
+          wait_vmcnt<IPG + KS>();  // page j's V DMA and K loads have landed
+        } else {
+          wait_vmcnt<0>();
+        }
+        compute(j, ka, B0{});
+        if (j + 1 >= n) break;
+        if (j + 2 < n) {
+          issue(j + 2, ka, B0{});
+          wait_vmcnt<IPG + KS>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        compute(j + 1, kb, B1{});
+      }
+
+      // the four lane groups hold disjoint keys of each head
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+      // accumulator row i of block db is dim 16db + 4grp + i
+      const bool whole = p0 == 0 && n == pages;
+      const int64_t slot = int64_t(g) * 2 + (first ? 0 : 1);
+      if (head_ok) {
+        if (whole) {
+          const float inv = 1.f / l;
+          float* op = a.out + (int64_t(tok) * a.hq + int64_t(kvh) * G + hq) * D + 4 * grp;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            *reinterpret_cast<float4*>(op + 16 * db) =
+                make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+        } else {
+          float* po = w.part_o + (slot * G + hq) * D + 4 * grp;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            *reinterpret_cast<float4*>(po + 16 * db) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
+          if (grp == 0) w.part_ml[slot * G + hq] = make_float2(m, l);
+        }
+      }
+
+      x += n;
+      first = false;
+      if (x < x_end) {  // next (row, kv head)
+        p0 = 0;
+        if (++kvh == a.hkv) {
+          kvh = 0;
+          rec = w.rows[++r];
+          base = w.rows_base[r];
+          pages = (rec.z + kBlock - 1) / kBlock;
+        }
+      }
+    }
+  }
+}
+
+template <int D, int G>
+int resident_waves_t() {
+  static int per_cu = 0;  // resident workgroups per CU, from the occupancy calculator
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<D, G>, kThreads, 0) != hipSuccess || n <= 0)
+      n = 1;
+    per_cu = n;
+  }
+  const int waves = device_cus() * per_cu * kWaves;
+  const int cap = device_cus() * kMaxWavesPerCU;
+  return waves < cap ? waves : cap;
+}
+
+template <int D, int G>
+hipError_t launch_t(const AttnArgs& a, const Workspace& w, hipStream_t st) {
+  int64_t waves = resident_waves_t<D, G>();
+  if (waves > w.ranges_cap) waves = w.ranges_cap;
+  const int64_t grid = (waves + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL((decode_mfma_kernel<D, G>), dim3(unsigned(grid)), dim3(kThreads), 0, st, a, w);
+  return hipGetLastError();
+}
+
+template <int D>
+int waves_d(int group) {
+  switch (group) {
+    case 1: return resident_waves_t<D, 1>();
+    case 2: return resident_waves_t<D, 2>();
+    case 4: return resident_waves_t<D, 4>();
+    case 8: return resident_waves_t<D, 8>();
+    default: return 1;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs& a, const Workspace& w, int group, hipStream_t st) {
+  switch (group) {
+    case 1: return launch_t<D, 1>(a, w, st);
+    case 2: return launch_t<D, 2>(a, w, st);
+    case 4: return launch_t<D, 4>(a, w, st);
+    case 8: return launch_t<D, 8>(a, w, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int decode_mfma_waves(int head_dim, int group) { return head_dim == 64 ? waves_d<64>(group) : waves_d<128>(group); }
+
+hipError_t launch_decode_mfma(const AttnArgs& a, const Workspace& w, int group, hipStream_t st) {
+  return a.d == 64 ? launch_d<64>(a, w, group, st) : launch_d<128>(a, w, group, st);
+}
+
+}  // namespace pa

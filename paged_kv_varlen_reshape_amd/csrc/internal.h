@@ -105,6 +105,11 @@ hipError_t launch_decode(const AttnArgs& a, const Workspace& w, int group, hipSt
 int decode_waves(int bf16, int head_dim, int group);
 // Page buffers per decode wavefront (option, else by group size).
 int decode_buffers(int group);
+// The bf16 MFMA decode kernel (decode_mfma.hip).
+hipError_t launch_decode_mfma(const AttnArgs& a, const Workspace& w, int group, hipStream_t st);
+int decode_mfma_waves(int head_dim, int group);
+// Row-wise decode runs on the MFMA kernel (option, else bf16).
+bool decode_uses_mfma(int bf16);
 hipError_t launch_merge(const AttnArgs& a, const Workspace& w, int group, hipStream_t st);
 hipError_t launch_chunk(const AttnArgs& a, const Workspace& w, int group, hipStream_t st);
 bool chunk_supported(int head_dim, int group, int bf16);

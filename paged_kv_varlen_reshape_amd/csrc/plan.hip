@@ -167,22 +167,34 @@ plan_kernel(PlanArgs a, Workspace w) {
   }
   __syncthreads();  // row records written above are read by other threads below
 
-  // pass 2, one thread per (row, kv head): every range start names the row
-  // holding it and, if it is the first boundary inside the pair, the pair
+  // pass 2: every range start names the row holding it and, if it is the
+  // first boundary inside a (row, kv head) pair, the pair
   const double inv_per = 1.0 / double(per);
-  for (int64_t pr = tid; pr < rows * hkv; pr += kPlanThreads) {
-    const int64_t r = pr / hkv;
-    const int k = int(pr - r * hkv);
-    const int64_t pages = (w.rows[r].z + kBlock - 1) / kBlock;
-    const int64_t start = w.rows_base[r] + k * pages;  // first unit of (r, k)
-    // first range whose start lies in [start, start + pages)
-    int64_t g = int64_t(double(start) * inv_per);
+  // range starts inside the unit run [start, start + pages) of pair (r, k)
+  auto mark_pair = [&](int64_t r, int k, int64_t start, int64_t pages) {
+    int64_t g = int64_t(double(start) * inv_per);  // first range starting at or after start
     while (g * per < start) ++g;
     while (g > 0 && (g - 1) * per >= start) --g;
     for (; g * per < start + pages && g < nranges; ++g) {
       const bool cut = g * per > start && (g - 1) * per <= start;  // first boundary strictly inside
       w.range_row[g] = int32_t(r);
       w.range_cut[g] = cut ? make_int2(int32_t(r), k) : make_int2(-1, -1);
+    }
+  };
+  if (rows * hkv <= kPlanThreads) {
+    // one thread per (row, kv head)
+    for (int64_t pr = tid; pr < rows * hkv; pr += kPlanThreads) {
+      const int64_t r = pr / hkv;
+      const int k = int(pr - r * hkv);
+      const int64_t pages = (w.rows[r].z + kBlock - 1) / kBlock;
+      mark_pair(r, k, w.rows_base[r] + k * pages, pages);
+    }
+  } else {
+    // one thread per row (its loads once, its kv heads in a loop)
+    for (int64_t r = tid; r < rows; r += kPlanThreads) {
+      const int64_t pages = (w.rows[r].z + kBlock - 1) / kBlock;
+      const int64_t b = w.rows_base[r];
+      for (int k = 0; k < hkv; ++k) mark_pair(r, k, b + k * pages, pages);
     }
   }
 

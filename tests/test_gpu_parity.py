@@ -42,6 +42,8 @@ def _reset_options():
     pk.pa_set_option(pk.PA_OPT_FORCE_ROWWISE, 0)
     pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, 0)
     pk.pa_set_option(pk.PA_OPT_TARGET_ITEMS, 0)
+    pk.pa_set_option(pk.PA_OPT_DECODE_BUFFERS, 0)
+    pk.pa_set_option(pk.PA_OPT_DECODE_KERNEL, 0)
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3])
@@ -99,6 +101,30 @@ def test_attention_random_steps(seed):
         pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, split)
         out = ds.attention()
         _check_attention(spec, ds, out)
+
+
+@pytest.mark.parametrize("kernel,nbuf", [(1, 1), (1, 2), (2, 0)])
+@pytest.mark.parametrize("seed", [100, 101, 102, 103])
+def test_bf16_decode_kernels_match_oracle(seed, kernel, nbuf):
+    """Both row-wise kernels for bf16 (VALU with one or two page buffers, MFMA),
+    every group size, ranges both shorter and longer than a row."""
+    r = np.random.default_rng(seed)
+    hkv = [1, 2, 4, 2][seed % 4]
+    g = [1, 2, 4, 8][seed % 4]
+    d = [64, 128][(seed // 2) % 2]
+    spec = W.random_spec(seed, num_seqs=int(r.integers(3, 9)), max_context=int(r.integers(40, 400)),
+                         max_query=int(r.integers(2, 24)), num_q_heads=hkv * g, num_kv_heads=hkv, head_dim=d,
+                         dtype="bf16", prefix_tokens=16, decode_fraction=0.6)
+    print(f"bf16 decode kernel={kernel} nbuf={nbuf} seed={seed} hkv={hkv} g={g} d={d}", flush=True)
+    ds = build_device_step(spec)
+    ds.reshape()
+    pk.pa_set_option(pk.PA_OPT_DECODE_KERNEL, kernel)
+    pk.pa_set_option(pk.PA_OPT_DECODE_BUFFERS, nbuf)
+    for rowwise in (0, 1):
+        pk.pa_set_option(pk.PA_OPT_FORCE_ROWWISE, rowwise)
+        for split in (0, 16, 80):
+            pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, split)
+            _check_attention(spec, ds, ds.attention())
 
 
 def test_forced_rowwise_and_split_sizes_agree():
