@@ -103,6 +103,11 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t
  *   query_start_loc  [num_seqs+1] int32, non-decreasing, last = num_tokens
  *   context_lens     [num_seqs] int32, cached tokens before this step
  *   out              [num_tokens, num_q_heads, head_dim] float32
+ *   max_query_len    (host) the longest query of the step, as a scheduler
+ *                    knows it; only <= 1 versus > 1 is used: <= 1 routes every
+ *                    row to the row-wise kernel and skips the chunk kernel's
+ *                    launch.  A wrong value changes which kernel computes a
+ *                    row, never the result; pass num_tokens if unknown
  *   workspace        device buffer of at least
  *                    pa_attention_workspace_size(...) bytes, 256-B aligned
  * The new K/V of the step must already be in the caches (call
@@ -115,8 +120,8 @@ int pa_attention(const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* query_start_loc, const int32_t* context_lens, float scale,
                  float* out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                 int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype,
-                 void* workspace, size_t workspace_bytes, void* stream);
+                 int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                 int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Check step metadata on host copies, O(num_tokens + num_seqs*max_blocks).
  *   seq_lens[i] == context_lens[i] + (query_start_loc[i+1]-query_start_loc[i]) >= 0,

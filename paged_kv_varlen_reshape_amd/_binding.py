@@ -40,7 +40,7 @@ SIGNATURES = {
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pa_attention_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_attention": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32,
-                            _i32, _i64, _i32, _i32, _vp, _sz, _vp]),
+                            _i32, _i64, _i32, _i32, _i32, _vp, _sz, _vp]),
     "pa_validate_metadata": (_i32, [_pi32, _pi32, _pi32, _pi32, _pi32, _i32, _i32, _i32, _i64, _i32]),
     "pa_last_error": (C.c_char_p, []),
     "pa_set_option": (_i32, [_i32, _i64]),
@@ -154,8 +154,10 @@ def pa_attention_workspace_size(num_seqs: int, num_tokens: int, num_q_heads: int
 
 
 def pa_attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens, scale: float,
-                 out=None, workspace=None):
-    """Attention of the step's query rows q [T, Hq, D] over the paged caches; returns out [T, Hq, D] fp32."""
+                 out=None, workspace=None, max_query_len=None):
+    """Attention of the step's query rows q [T, Hq, D] over the paged caches; returns out [T, Hq, D] fp32.
+
+    max_query_len: the step's longest query as the caller knows it (host int); None passes T (unknown)."""
     import torch
 
     T, hq, d = q.shape
@@ -174,7 +176,8 @@ def pa_attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, c
     _check(lib().pa_attention(_dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
                               _dev_ptr(block_tables, "block_tables"), _dev_ptr(seq_lens, "seq_lens"),
                               _dev_ptr(query_start_loc, "query_start_loc"), _dev_ptr(context_lens, "context_lens"),
-                              float(scale), _dev_ptr(out, "out"), S, T, hq, hkv, d, bs, nb, mbps, _dtype_code(q),
+                              float(scale), _dev_ptr(out, "out"), S, T, hq, hkv, d, bs, nb, mbps,
+                              T if max_query_len is None else int(max_query_len), _dtype_code(q),
                               _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                               _stream_handle(q.device)))
     return out

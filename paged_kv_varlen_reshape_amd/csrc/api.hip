@@ -162,8 +162,8 @@ extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_ca
                             const int32_t* seq_lens, const int32_t* query_start_loc, const int32_t* context_lens,
                             float scale, float* out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                            int32_t max_blocks_per_seq, int32_t dtype, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+                            int32_t max_blocks_per_seq, int32_t max_query_len, int32_t dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   clear_error();
   if (int rc = check_dims(num_kv_heads, head_dim, block_size, dtype, num_blocks, "pa_attention")) return rc;
   if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
@@ -179,6 +179,8 @@ extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_ca
   if (max_blocks_per_seq == 0) return fail(PA_ERR_INVALID, "pa_attention: max_blocks_per_seq is 0 with query rows");
   if (int64_t(max_blocks_per_seq) * kBlock >= (int64_t(1) << 31))
     return fail(PA_ERR_INVALID, "pa_attention: max_blocks_per_seq too large");
+  if (int64_t(num_kv_heads) * max_blocks_per_seq >= (int64_t(1) << 31))  // one row's pages over all kv heads
+    return fail(PA_ERR_INVALID, "pa_attention: num_kv_heads * max_blocks_per_seq too large");
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !context_lens || !out)
     return fail(PA_ERR_INVALID, "pa_attention: null pointer");
   StepShape shape{num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq};
@@ -190,7 +192,8 @@ extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_ca
 
   const Workspace w = layout_workspace(shape, workspace);
   const bool bf16 = dtype == PA_BF16;
-  const bool use_mfma = !option(PA_OPT_FORCE_ROWWISE) && chunk_supported(head_dim, group, bf16);
+  // a decode-only step (every query of length <= 1) has no chunk tiles
+  const bool use_mfma = !option(PA_OPT_FORCE_ROWWISE) && max_query_len > 1 && chunk_supported(head_dim, group, bf16);
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   PlanArgs pa_args{};
@@ -244,7 +247,8 @@ extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_ca
   }
   if (e == hipSuccess) {
     KernelTimer t(PA_K_MERGE, st);
-    e = launch_merge(a, w, group, st);
+    // automatic ranges number at most num_ranges; fixed-length ones up to the capacity
+    e = launch_merge(a, w, group, pa_args.fixed_units > 0 ? w.ranges_cap : pa_args.num_ranges, st);
   }
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_attention: launch failed: %s", hipGetErrorString(e));
   return PA_OK;

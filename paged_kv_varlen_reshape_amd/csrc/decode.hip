@@ -411,10 +411,11 @@ hipError_t launch_decode_t(const AttnArgs& a, const Workspace& w, hipStream_t st
 }
 
 template <int D, int G>
-hipError_t launch_merge_t(const AttnArgs& a, const Workspace& w, hipStream_t st) {
+hipError_t launch_merge_t(const AttnArgs& a, const Workspace& w, int64_t max_ranges, hipStream_t st) {
   // one wavefront per range: each merge is a short chain of dependent loads,
   // so they all run side by side (a range without a cut exits at once)
-  const int64_t grid = (w.ranges_cap + 3) / 4;
+  if (max_ranges > w.ranges_cap) max_ranges = w.ranges_cap;
+  const int64_t grid = (max_ranges + 3) / 4;
   hipLaunchKernelGGL((split_merge_kernel<D, G>), dim3(unsigned(grid)), dim3(256), 0, st, a, w);
   return hipGetLastError();
 }
@@ -452,12 +453,12 @@ hipError_t launch_decode_d(const AttnArgs& a, const Workspace& w, int group, int
 }
 
 template <int D>
-hipError_t launch_merge_d(const AttnArgs& a, const Workspace& w, int group, hipStream_t st) {
+hipError_t launch_merge_d(const AttnArgs& a, const Workspace& w, int group, int64_t mr, hipStream_t st) {
   switch (group) {
-    case 1: return launch_merge_t<D, 1>(a, w, st);
-    case 2: return launch_merge_t<D, 2>(a, w, st);
-    case 4: return launch_merge_t<D, 4>(a, w, st);
-    case 8: return launch_merge_t<D, 8>(a, w, st);
+    case 1: return launch_merge_t<D, 1>(a, w, mr, st);
+    case 2: return launch_merge_t<D, 2>(a, w, mr, st);
+    case 4: return launch_merge_t<D, 4>(a, w, mr, st);
+    case 8: return launch_merge_t<D, 8>(a, w, mr, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -490,8 +491,8 @@ hipError_t launch_decode(const AttnArgs& a, const Workspace& w, int group, hipSt
   return a.d == 64 ? launch_decode_d<false, 64>(a, w, group, nbuf, st) : launch_decode_d<false, 128>(a, w, group, nbuf, st);
 }
 
-hipError_t launch_merge(const AttnArgs& a, const Workspace& w, int group, hipStream_t st) {
-  return a.d == 64 ? launch_merge_d<64>(a, w, group, st) : launch_merge_d<128>(a, w, group, st);
+hipError_t launch_merge(const AttnArgs& a, const Workspace& w, int group, int64_t max_ranges, hipStream_t st) {
+  return a.d == 64 ? launch_merge_d<64>(a, w, group, max_ranges, st) : launch_merge_d<128>(a, w, group, max_ranges, st);
 }
 
 }  // namespace pa

@@ -110,7 +110,8 @@ hipError_t launch_decode_mfma(const AttnArgs& a, const Workspace& w, int group, 
 int decode_mfma_waves(int head_dim, int group);
 // Row-wise decode runs on the MFMA kernel (option, else bf16).
 bool decode_uses_mfma(int bf16);
-hipError_t launch_merge(const AttnArgs& a, const Workspace& w, int group, hipStream_t st);
+// max_ranges: an upper bound on the plan's range count (sizes the grid)
+hipError_t launch_merge(const AttnArgs& a, const Workspace& w, int group, int64_t max_ranges, hipStream_t st);
 hipError_t launch_chunk(const AttnArgs& a, const Workspace& w, int group, hipStream_t st);
 bool chunk_supported(int head_dim, int group, int bf16);
 int chunk_tile_rows(int group);

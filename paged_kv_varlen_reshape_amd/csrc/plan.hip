@@ -11,12 +11,11 @@
 // pages per kv head; all those (row, kv head, page) units form one stream
 // that is cut into equal ranges, one per decode wavefront.
 //
-// One workgroup of 1024 threads.  Pass 1 walks the sequences in chunks of
-// 1024 with block scans that place every tile record, row record and row's
-// first unit; the tiles are then sorted longest first; pass 2 walks the rows
-// and marks, for every range, the row holding its first unit and the (row, kv
-// head) it cuts.  It also clears the
-// work counter the chunk kernel uses.
+// One workgroup of 1024 threads.  Pass 1 gives each thread a contiguous run of
+// sequences and places every tile record, row record and row's first unit
+// with one block scan; the tiles are then sorted longest first; pass 2 marks,
+// for every range, the row holding its first unit and the (row, kv head) it
+// cuts.  It also clears the work counter the chunk kernel uses.
 #include "internal.h"
 
 namespace pa {
@@ -25,6 +24,8 @@ namespace {
 constexpr int kWavesPerPlan = kPlanThreads / kWave;
 constexpr int kSortBuckets = kPlanThreads;  // key-count buckets of the tile sort, one per thread
 constexpr int kSortBucketKeys = 64;         // keys per bucket (one chunk-kernel key tile)
+constexpr int kSeqBatch = 4;                // sequences whose metadata loads are issued together
+constexpr int kLdsRows = 8192;              // rows whose first units the range search keeps in LDS
 
 // Exclusive scans of two non-negative int64 at once (one set of barriers).
 __device__ void block_exclusive_scan2(int64_t x, int64_t y, int64_t* ox, int64_t* oy, int64_t* tx, int64_t* ty,
@@ -72,69 +73,87 @@ struct SeqInfo {
   bool chunk;
 };
 
-__device__ __forceinline__ SeqInfo seq_info(const PlanArgs& a, int i) {
-  SeqInfo s{0, 0, 0, false};
-  if (i >= a.num_seqs) return s;
-  int32_t r0 = a.qsl[i];
-  int32_t q = a.qsl[i + 1] - r0;
-  int32_t c = a.ctx[i];
-  // metadata is trusted, but nothing below may index outside the arrays
-  if (q < 0) q = 0;
-  if (r0 < 0 || r0 >= a.num_tokens) q = 0;
-  if (q > a.num_tokens - r0) q = a.num_tokens - r0;
-  if (c < 0) c = 0;
+// Sequence i's rows, clamped so that nothing below indexes outside the
+// arrays (metadata is trusted).  Branch-free: an index past the last
+// sequence (valid == false) loads sequence 0 and yields no rows, so a batch of
+// calls issues all its loads at once.
+__device__ __forceinline__ SeqInfo seq_info(const PlanArgs& a, int64_t i, bool valid) {
+  const int j = valid ? int(i) : 0;
+  const int32_t r0 = a.qsl[j];
+  int32_t q = a.qsl[j + 1] - r0;
+  int32_t c = a.ctx[j];
+  q = int32_t(min(int64_t(max(q, 0)), int64_t(a.num_tokens) - r0));
+  if (!valid || r0 < 0 || r0 >= a.num_tokens) q = 0;
+  c = max(c, 0);
   if (int64_t(c) + q > a.max_len) q = c >= a.max_len ? 0 : a.max_len - c;
-  s.r0 = r0;
-  s.q = q;
-  s.c = c;
-  s.chunk = q > 1 && a.use_mfma;
-  return s;
+  return SeqInfo{r0, q, c, q > 1 && a.use_mfma};
+}
+
+__device__ __forceinline__ void seq_counts(const SeqInfo& s, int tile_rows, int64_t hkv, int64_t& ntile,
+                                           int64_t& nrow, int64_t& nunit) {
+  if (s.chunk) {
+    ntile += (s.q + tile_rows - 1) / tile_rows;
+  } else if (s.q > 0) {
+    nrow += s.q;
+    nunit += hkv * (pages_upto(int64_t(s.c) + s.q) - pages_upto(s.c));
+  }
 }
 
 __global__ void __launch_bounds__(kPlanThreads)
 plan_kernel(PlanArgs a, Workspace w) {
   __shared__ int64_t sh[2 * kWavesPerPlan];
   __shared__ int s_hist[kSortBuckets];
+  __shared__ int64_t s_base[kLdsRows];   // first unit of each row
+  __shared__ int32_t s_pages[kLdsRows];  // pages of each row (per kv head)
   const int tid = threadIdx.x;
   const int64_t hkv = a.num_kv_heads;
 
-  // pass 1: scans place the tile records, the row records (packed high/low
-  // words of one value) and each row's first unit
-  int64_t tiles = 0, rows = 0, units = 0;
-  for (int base = 0; base < a.num_seqs; base += kPlanThreads) {
-    const int i = base + tid;
-    const SeqInfo s = seq_info(a, i);
-    int64_t ntile = 0, nrow = 0, nunit = 0;
-    if (s.chunk) {
-      ntile = (s.q + a.tile_rows - 1) / a.tile_rows;
-    } else if (s.q > 0) {
-      nrow = s.q;
-      nunit = hkv * (pages_upto(int64_t(s.c) + s.q) - pages_upto(s.c));
+  // pass 1: thread t owns the contiguous sequences [i0, i1); one scan of the
+  // per-thread counts places its tile records, row records and units
+  const int64_t m = (int64_t(a.num_seqs) + kPlanThreads - 1) / kPlanThreads;
+  const int64_t i0 = min(int64_t(tid) * m, int64_t(a.num_seqs)), i1 = min(i0 + m, int64_t(a.num_seqs));
+  int64_t ntile = 0, nrow = 0, nunit = 0;
+  for (int64_t ib = i0; ib < i1; ib += kSeqBatch) {
+#pragma unroll
+    for (int c = 0; c < kSeqBatch; ++c)
+      seq_counts(seq_info(a, ib + c, ib + c < i1), a.tile_rows, hkv, ntile, nrow, nunit);
+  }
+  int64_t off_tr, off_u, tot_tr, tot_u;
+  block_exclusive_scan2((ntile << 32) | nrow, nunit, &off_tr, &off_u, &tot_tr, &tot_u, sh);
+  int64_t tiles = tot_tr >> 32, rows = tot_tr & 0xFFFFFFFFll;
+  const int64_t units = tot_u;
+  {
+    int64_t t = off_tr >> 32, r = off_tr & 0xFFFFFFFFll, u = off_u;
+    for (int64_t ib = i0; ib < i1; ib += kSeqBatch) {
+#pragma unroll
+      for (int c = 0; c < kSeqBatch; ++c) {
+        const SeqInfo s = seq_info(a, ib + c, ib + c < i1);
+        if (s.chunk) {
+          // tile records with their key count (bucketed in kSortBucketKeys) for the sort below
+          for (int32_t first = 0; first < s.q && t < w.tiles_cap; first += a.tile_rows, ++t) {
+            const int32_t nt = min(a.tile_rows, s.q - first);
+            const int64_t bucket = (int64_t(s.c) + first + nt) / kSortBucketKeys;
+            w.tiles_tmp[t] = make_int4(int(ib + c), first, int32_t(bucket < kSortBuckets ? bucket : kSortBuckets - 1), 0);
+          }
+        } else {
+          for (int32_t j = 0; j < s.q && r < w.rows_cap; ++j, ++r) {
+            const int32_t len = s.c + j + 1;
+            const int32_t pages = (len + kBlock - 1) / kBlock;
+            w.rows[r] = make_int4(s.r0 + j, int(ib + c), len, 0);
+            w.rows_base[r] = u;
+            if (r < kLdsRows) {
+              s_base[r] = u;
+              s_pages[r] = pages;
+            }
+            u += hkv * pages;
+          }
+        }
+      }
     }
-    int64_t off_tr, off_u, tot_tr, tot_u;
-    block_exclusive_scan2((ntile << 32) | nrow, nunit, &off_tr, &off_u, &tot_tr, &tot_u, sh);
-    const int64_t t0 = tiles + (off_tr >> 32), r0 = rows + (off_tr & 0xFFFFFFFFll);
-    // tile records with their key count (bucketed in kSortBucketKeys) for the sort below
-    for (int64_t t = 0; t < ntile && t0 + t < w.tiles_cap; ++t) {
-      const int32_t first = int32_t(t) * a.tile_rows;
-      const int32_t nt = min(a.tile_rows, s.q - first);
-      const int64_t bucket = (int64_t(s.c) + first + nt) / kSortBucketKeys;
-      w.tiles_tmp[t0 + t] = make_int4(i, first, int32_t(bucket < kSortBuckets ? bucket : kSortBuckets - 1), 0);
-    }
-    int64_t u = units + off_u;
-    for (int32_t j = 0; j < nrow && r0 + j < w.rows_cap; ++j) {
-      const int32_t len = s.c + j + 1;
-      w.rows[r0 + j] = make_int4(s.r0 + j, i, len, 0);
-      w.rows_base[r0 + j] = u;
-      u += hkv * ((len + kBlock - 1) / kBlock);
-    }
-    tiles += tot_tr >> 32;
-    rows += tot_tr & 0xFFFFFFFFll;
-    units += tot_u;
   }
   if (tiles > w.tiles_cap) tiles = w.tiles_cap;  // only with inconsistent metadata
   if (rows > w.rows_cap) rows = w.rows_cap;
-  __syncthreads();  // tile records written above are read by other threads below
+  __syncthreads();  // tile and row records written above are read by other threads below
 
   // chunk tiles longest first (counting sort on key count, descending), so
   // the tiles that see the most keys start first and the tail stays short;
@@ -165,36 +184,41 @@ plan_kernel(PlanArgs a, Workspace w) {
     per = (units + w.ranges_cap - 1) / w.ranges_cap;
     nranges = (units + per - 1) / per;
   }
-  __syncthreads();  // row records written above are read by other threads below
 
   // pass 2: every range start names the row holding it and, if it is the
-  // first boundary inside a (row, kv head) pair, the pair
-  const double inv_per = 1.0 / double(per);
-  // range starts inside the unit run [start, start + pages) of pair (r, k)
-  auto mark_pair = [&](int64_t r, int k, int64_t start, int64_t pages) {
-    int64_t g = int64_t(double(start) * inv_per);  // first range starting at or after start
-    while (g * per < start) ++g;
-    while (g > 0 && (g - 1) * per >= start) --g;
-    for (; g * per < start + pages && g < nranges; ++g) {
-      const bool cut = g * per > start && (g - 1) * per <= start;  // first boundary strictly inside
-      w.range_row[g] = int32_t(r);
-      w.range_cut[g] = cut ? make_int2(int32_t(r), k) : make_int2(-1, -1);
-    }
-  };
-  if (rows * hkv <= kPlanThreads) {
-    // one thread per (row, kv head)
-    for (int64_t pr = tid; pr < rows * hkv; pr += kPlanThreads) {
-      const int64_t r = pr / hkv;
-      const int k = int(pr - r * hkv);
-      const int64_t pages = (w.rows[r].z + kBlock - 1) / kBlock;
-      mark_pair(r, k, w.rows_base[r] + k * pages, pages);
+  // first boundary strictly inside a (row, kv head) pair, the pair.  A start
+  // `off` units into its pair is that boundary iff 0 < off <= per.
+  if (rows <= kLdsRows) {
+    // one thread per range: binary search of the rows' first units in LDS
+    for (int64_t g = tid; g < nranges; g += kPlanThreads) {
+      const int64_t start = g * per;
+      int lo = 0, hi = int(rows);  // s_base[lo] <= start < s_base[hi] (hi == rows: end of stream)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_base[mid] <= start) lo = mid;
+        else hi = mid;
+      }
+      const uint32_t rel = uint32_t(start - s_base[lo]), pages = uint32_t(s_pages[lo]);
+      const uint32_t k = rel / pages, off = rel - k * pages;
+      w.range_row[g] = lo;
+      w.range_cut[g] = off > 0 && off <= per ? make_int2(lo, int(k)) : make_int2(-1, -1);
     }
   } else {
-    // one thread per row (its loads once, its kv heads in a loop)
+    // one thread per row: the range starts inside each of its pairs
+    const double inv_per = 1.0 / double(per);
     for (int64_t r = tid; r < rows; r += kPlanThreads) {
       const int64_t pages = (w.rows[r].z + kBlock - 1) / kBlock;
-      const int64_t b = w.rows_base[r];
-      for (int k = 0; k < hkv; ++k) mark_pair(r, k, b + k * pages, pages);
+      for (int k = 0; k < hkv; ++k) {
+        const int64_t start = w.rows_base[r] + k * pages;
+        int64_t g = int64_t(double(start) * inv_per);  // first range starting at or after start
+        while (g * per < start) ++g;
+        while (g > 0 && (g - 1) * per >= start) --g;
+        for (; g * per < start + pages && g < nranges; ++g) {
+          const int64_t off = g * per - start;
+          w.range_row[g] = int32_t(r);
+          w.range_cut[g] = off > 0 && off <= per ? make_int2(int32_t(r), k) : make_int2(-1, -1);
+        }
+      }
     }
   }
 

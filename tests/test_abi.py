@@ -74,7 +74,8 @@ def test_attention_rejects_bad_arguments():
         need = lib.pa_attention_workspace_size(S, T, hq, hkv, d, mbps)
         wsb = need if ws_bytes is None else ws_bytes
         p = ptr
-        return lib.pa_attention(p, p, p, p, p, p, p, scale, p, S, T, hq, hkv, d, bs, nb, mbps, dtype, ws, wsb, None)
+        return lib.pa_attention(p, p, p, p, p, p, p, scale, p, S, T, hq, hkv, d, bs, nb, mbps, T, dtype, ws, wsb,
+                                None)
 
     assert call(hq=6, hkv=4) == pk.PA_ERR_INVALID
     assert call(hq=32, hkv=2) == pk.PA_ERR_UNSUPPORTED  # group 16 is not built

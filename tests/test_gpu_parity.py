@@ -127,6 +127,40 @@ def test_bf16_decode_kernels_match_oracle(seed, kernel, nbuf):
             _check_attention(spec, ds, ds.attention())
 
 
+def test_many_sequences_plan_fallbacks():
+    """More sequences than the plan keeps in registers and more rows than its
+    LDS range search holds: both fallback paths, checked on sampled sequences."""
+    spec = W.random_spec(40, num_seqs=9000, max_context=70, max_query=3, num_q_heads=4, num_kv_heads=2,
+                         head_dim=64, dtype="f32", decode_fraction=0.3)
+    assert spec.num_tokens > 8192
+    print(f"many sequences: {spec.num_seqs} seqs, {spec.num_tokens} rows", flush=True)
+    ds = build_device_step(spec)
+    ds.reshape()
+    seqs = sorted(np.random.default_rng(40).choice(spec.num_seqs, 200, replace=False).tolist()) + [spec.num_seqs - 1]
+    for split in (0, 16):
+        pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, split)
+        _check_attention(spec, ds, ds.attention(), seqs)
+
+
+def test_max_query_len_hint_never_changes_results():
+    """<= 1 sends every row to the row-wise kernel: exact for a decode step,
+    within tolerance (other kernel) for a mixed step given a wrong hint."""
+    dec = build_device_step(W.make_config(2))
+    dec.reshape()
+    a = dec.attention().clone()
+    b = pk.pa_attention(dec.q, dec.k_cache, dec.v_cache, dec.block_tables, dec.seq_lens, dec.query_start_loc,
+                        dec.context_lens, dec.spec.scale, max_query_len=dec.q.shape[0])
+    torch.cuda.synchronize()
+    assert dec.max_query_len == 1 and torch.equal(a, b)
+    spec = W.make_config(3)
+    mix = build_device_step(spec)
+    mix.reshape()
+    assert mix.max_query_len > 1
+    out = pk.pa_attention(mix.q, mix.k_cache, mix.v_cache, mix.block_tables, mix.seq_lens, mix.query_start_loc,
+                          mix.context_lens, spec.scale, max_query_len=1)
+    _check_attention(spec, mix, out)
+
+
 def test_forced_rowwise_and_split_sizes_agree():
     spec = W.make_config(3)
     ds = build_device_step(spec)

@@ -45,13 +45,17 @@ class DeviceStep:
     query_start_loc: torch.Tensor
     context_lens: torch.Tensor
 
+    @property
+    def max_query_len(self) -> int:
+        return max((r.query for r in self.spec.requests), default=0)
+
     def reshape(self):
         pk.pa_reshape_and_cache(self.k_new, self.v_new, self.slot_mapping, self.k_cache, self.v_cache)
 
     def attention(self, out=None, workspace=None):
         return pk.pa_attention(self.q, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
                                self.query_start_loc, self.context_lens, self.spec.scale, out=out,
-                               workspace=workspace)
+                               workspace=workspace, max_query_len=self.max_query_len)
 
     def workspace(self):
         s = self.spec
