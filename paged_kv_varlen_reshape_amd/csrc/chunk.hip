@@ -66,6 +66,12 @@ using I1 = std::integral_constant<int, 1>;
 constexpr int kTileRows = 128;  // query rows per workgroup tile
 constexpr int kBN = 64;         // keys per K/V tile
 constexpr int kThreads = 256;
+constexpr int KLOOK = 2;  // K operand reads in flight ahead of the Q.K products
+
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -184,12 +190,12 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
     // block id of this wavefront's page in tile kt (raw: made wave-uniform and
     // clamped where it is used, a tile later, so its load is not waited for here
     // -- vector loads retire in order, so that wait would also wait for the DMA)
-    auto page_id = [&](int kt) -> int32_t {
+    auto page_id = [&](int kt) __attribute__((always_inline)) -> int32_t {
       const int page = kt * 4 + wave;
       return page < n_pages ? btrow[page] : 0;
     };
     // DMA of this wavefront's page of tile kt into buffer buf (nothing past the sequence)
-    auto dma_tile = [&](int kt, auto bufc, int32_t raw) {
+    auto dma_tile = [&](int kt, auto bufc, int32_t raw) __attribute__((always_inline)) {
       constexpr int buf = decltype(bufc)::value;
       char* dk = buf ? s_k1 : s_k0;
       char* dv = buf ? s_v1 : s_v0;
@@ -208,7 +214,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
       }
     };
     // after the DMA has landed: V rows of keys at or past kv_end become zeros
-    auto zero_tail = [&](int kt, auto bufc) {
+    auto zero_tail = [&](int kt, auto bufc) __attribute__((always_inline)) {
       char* dv = decltype(bufc)::value ? s_v1 : s_v0;
       const int key0 = kt * kBN + wave * kBlock;  // first key of this wavefront's page
       if (key0 + kBlock <= kv_end) return;
@@ -229,7 +235,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
 
     // tiles below n_full are visible to every row of the tile: no mask
     const int n_full = (ctx + t0 + 1) / kBN;
-    auto tile_step = [&](int kt, auto bufc, auto masked) {
+    auto tile_step = [&](int kt, auto bufc, auto masked) __attribute__((always_inline)) {
       constexpr int buf = decltype(bufc)::value;
       using Other = std::integral_constant<int, buf ^ 1>;
       // the next tile's DMA flies while this one is multiplied
@@ -253,6 +259,14 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
           s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), as_bf16x8(qf[kk]), s[0], 0, 0, 0);
           s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), as_bf16x8(qf[kk]), s[1], 0, 0, 0);
         }
+        // schedule: the operand reads run KLOOK steps ahead of the products
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * KLOOK, 0);
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS - KLOOK; ++kk) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * KLOOK, 0);
       }
       // causal mask (also hides keys past the tile's end): key > pos -> -inf;
       // accumulator row j of block mb is key key0 + lg*4 + mb*32 + (j/4)*8 + j%4
@@ -272,9 +286,12 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
 #pragma unroll
       for (int j = 1; j < 16; ++j) mx = fmaxf(mx, fmaxf(s[0][j], s[1][j]));
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-      if (mx > m + 8.f) {
-        const float alpha = fast_exp2(m - mx);  // 0 on the first tile (m = -inf)
-        m = mx;
+      // wave-uniform branch (rarely taken after the first tiles); lanes whose
+      // maximum did not grow scale by 1
+      const bool grow = mx > m + 8.f;
+      if (__any(grow)) {
+        const float alpha = grow ? fast_exp2(m - mx) : 1.f;  // 0 on the first tile (m = -inf)
+        m = grow ? mx : m;
         l *= alpha;
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
@@ -323,14 +340,18 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
       }
       __syncthreads();
     };
-    auto step = [&](int kt, auto masked) {
-      if (kt & 1)
-        tile_step(kt, I1{}, masked);
-      else
+    // tile kt sits in buffer kt & 1: two tiles per iteration keep the buffer
+    // choice static, so the accumulators flow through one path (no copies)
+    auto run = [&](int kt, int kt_end, auto masked) __attribute__((always_inline)) {
+      if ((kt & 1) && kt < kt_end) tile_step(kt++, I1{}, masked);
+      for (; kt + 1 < kt_end; kt += 2) {
         tile_step(kt, I0{}, masked);
+        tile_step(kt + 1, I1{}, masked);
+      }
+      if (kt < kt_end) tile_step(kt, I0{}, masked);
     };
-    for (int kt = 0; kt < min(n_full, n_kt); ++kt) step(kt, std::false_type{});
-    for (int kt = max(n_full, 0); kt < n_kt; ++kt) step(kt, std::true_type{});
+    run(0, min(n_full, n_kt), std::false_type{});
+    run(max(n_full, 0), n_kt, std::true_type{});
 
     // the two lane halves hold disjoint keys of the same row
     l += __shfl_xor(l, 32);
