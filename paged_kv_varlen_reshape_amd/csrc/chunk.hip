@@ -66,6 +66,9 @@ using I1 = std::integral_constant<int, 1>;
 constexpr int kTileRows = 128;  // query rows per workgroup tile
 constexpr int kBN = 64;         // keys per K/V tile
 constexpr int kThreads = 256;
+constexpr int kHandoverTiles = 4;  // the next item is claimed this many key tiles before the end
+
+typedef const __attribute__((address_space(4))) int32_t const_i32;  // read with scalar loads
 constexpr int KLOOK = 2;  // K operand reads in flight ahead of the Q.K products
 
 // instruction classes of __builtin_amdgcn_sched_group_barrier
@@ -145,23 +148,78 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
   const char* kbase = static_cast<const char*>(a.kc);
   const char* vbase = static_cast<const char*>(a.vc);
 
-  if (tid == 0) s_item = blockIdx.x;
-  __syncthreads();
-  int item = s_item;
-  while (item < n_items) {
-    __syncthreads();  // every thread has read s_item
-    if (tid == 0) s_item = int(gridDim.x) + atomicAdd(&w.hdr[H_COUNTER2], 1);
+  // Work queue: the workgroup's first item is blockIdx.x, later ones come from
+  // a counter (longest items first).  The next item is claimed a few key
+  // tiles before the current one ends (late enough to keep the queue's
+  // longest-first balance) and everything it needs before its first DMA is
+  // fetched at the following tile boundaries, one dependent scalar load per
+  // boundary, so an item starts with one memory latency instead of a chain.
+  const_i32* cqsl = (const_i32*)a.qsl;
+  const_i32* cctx = (const_i32*)a.ctx;
+  const_i32* ctiles = (const_i32*)w.tiles;  // int2 records {seq, first row}
+  const_i32* cbt = (const_i32*)a.bt;
+  struct Meta {
+    int seq, t0, r0, qend, ctx, blk0;  // blk0: block id of this wavefront's page of tile 0
+  };
+  // the item's tile record (stage 1), its sequence's rows (stage 2), its first block id (stage 3)
+  auto meta_stage1 = [&](int it, Meta& mt) __attribute__((always_inline)) {
+    if (it >= n_items) return;
+    const int tl = __builtin_amdgcn_readfirstlane(it / a.hkv);
+    mt.seq = ctiles[2 * tl];
+    mt.t0 = ctiles[2 * tl + 1];
+  };
+  auto meta_stage2 = [&](int it, Meta& mt) __attribute__((always_inline)) {
+    if (it >= n_items) return;
+    mt.r0 = cqsl[mt.seq];
+    mt.qend = cqsl[mt.seq + 1];
+    mt.ctx = cctx[mt.seq];
+  };
+  // the plan clamped the rows it tiled the same way: nothing may index
+  // outside q, out or the block-table row even with inconsistent metadata
+  auto tile_len = [&](const Meta& mt) __attribute__((always_inline)) -> int {
+    const int cx = max(mt.ctx, 0);
+    const int qlen = min(min(mt.qend - mt.r0, a.num_tokens - mt.r0), a.mbps * kBlock - cx);
+    return max(0, min(TQ, qlen - mt.t0));
+  };
+  auto meta_stage3 = [&](int it, Meta& mt) __attribute__((always_inline)) {
+    mt.blk0 = 0;
+    if (it >= n_items) return;
+    const int kv_end_n = max(mt.ctx, 0) + mt.t0 + tile_len(mt);
+    if (wave * kBlock < kv_end_n) mt.blk0 = cbt[int64_t(mt.seq) * a.mbps + wave];
+  };
 
-    const int tile = item / a.hkv;
-    const int kvh = item - tile * a.hkv;
-    const int2 trec = w.tiles[tile];
-    const int seq = trec.x, t0 = trec.y;
-    const int r0 = a.qsl[seq];
-    const int ctx = max(a.ctx[seq], 0);
-    // the plan clamped the rows it tiled the same way: nothing may index
-    // outside q, out or the block-table row even with inconsistent metadata
-    const int qlen = min(min(a.qsl[seq + 1] - r0, a.num_tokens - r0), a.mbps * kBlock - ctx);
-    const int nt = max(0, min(TQ, qlen - t0));  // valid tokens of this tile
+  int item = blockIdx.x;
+  Meta cur{};
+  meta_stage1(item, cur);
+  meta_stage2(item, cur);
+  meta_stage3(item, cur);
+  while (item < n_items) {
+    // the hand-over to the next item: phase 0 claims it (thread 0), phase 1
+    // publishes its number in LDS, phases 2 and 3 load its tile record and
+    // sequence rows; each phase runs at the start of one key tile, after the
+    // barrier that ended the tile before (which also waited for the phase
+    // before it), and what is left runs when the item ends
+    int claimed = 0, next = n_items, phase = 0;
+    Meta nxt{};
+    auto handover = [&]() __attribute__((always_inline)) {
+      if (phase == 0) {
+        if (tid == 0) claimed = int(gridDim.x) + atomicAdd(&w.hdr[H_COUNTER2], 1);
+      } else if (phase == 1) {
+        if (tid == 0) s_item = claimed;
+      } else if (phase == 2) {
+        next = __builtin_amdgcn_readfirstlane(s_item);
+        meta_stage1(next, nxt);
+      } else if (phase == 3) {
+        meta_stage2(next, nxt);
+      }
+      ++phase;
+    };
+
+    const int kvh = item - (item / a.hkv) * a.hkv;
+    const int seq = cur.seq, t0 = cur.t0;
+    const int r0 = cur.r0;
+    const int ctx = max(cur.ctx, 0);
+    const int nt = tile_len(cur);  // valid tokens of this tile
     const int kv_end = ctx + t0 + nt;           // keys seen by the tile's last row
     const int n_kt = (kv_end + kBN - 1) / kBN;
     const int n_pages = (kv_end + kBlock - 1) / kBlock;
@@ -225,19 +283,20 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
       }
     };
 
-    // prologue: tile 0 in buffer 0
-    int32_t id_next = page_id(0);
-    dma_tile(0, I0{}, id_next);
-    if (n_kt > 1) id_next = page_id(1);
+    // prologue: tile 0 in buffer 0 (its block id came with the item)
+    dma_tile(0, I0{}, cur.blk0);
+    int32_t id_next = n_kt > 1 ? page_id(1) : 0;
     __builtin_amdgcn_s_waitcnt(0);
     zero_tail(0, I0{});
     __syncthreads();
+    const int handover_from = n_kt - kHandoverTiles;  // key tile of phase 0
 
     // tiles below n_full are visible to every row of the tile: no mask
     const int n_full = (ctx + t0 + 1) / kBN;
     auto tile_step = [&](int kt, auto bufc, auto masked) __attribute__((always_inline)) {
       constexpr int buf = decltype(bufc)::value;
       using Other = std::integral_constant<int, buf ^ 1>;
+      if (kt >= handover_from) handover();
       // the next tile's DMA flies while this one is multiplied
       if (kt + 1 < n_kt) {
         dma_tile(kt + 1, Other{}, id_next);
@@ -368,8 +427,18 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
         }
     }
 
+    // phases a short item had no tiles for, each after a barrier
+    while (phase < 4) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      handover();
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    meta_stage3(next, nxt);
+    // every wavefront is done with the LDS tiles and has read s_item
     __syncthreads();
-    item = s_item;
+    item = next;
+    cur = nxt;
   }
 }
 
