@@ -107,13 +107,10 @@ def recorded_traffic(kernel: str, cfg_id: int):
     size) recorded under profiles/ for this kernel and workload, or None if there is
     no record or the kernel's sources changed since the counters were taken."""
     import glob
-    import hashlib
 
-    h = hashlib.sha256()
-    for f in ("decode.hip", "plan.hip", "internal.h"):
-        with open(os.path.join(ROOT, "paged_kv_varlen_reshape_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    sha = h.hexdigest()[:16]
+    from paged_kv_varlen_reshape_amd.traffic_record import sources_sha
+
+    sha = sources_sha(kernel)
     for path in glob.glob(os.path.join(ROOT, "profiles", "*.traffic.txt")):
         for line in open(path):
             if not line.startswith("traffic:"):
@@ -233,7 +230,10 @@ def main(argv=None):
     use_mfma = spec.dtype == "bf16" and pk.pa_get_option(pk.PA_OPT_FORCE_ROWWISE) == 0 and prof["chunk_mfma"][0] > 0
     work = algorithmic_work(spec, use_mfma)
     ms = dt * 1e3 / args.steps
-    decode_n, decode_ms = prof["decode_streamk"]
+    decode_n, decode_ms = prof["decode"]
+    # the row-wise kernel bf16 steps take unless an option picks the VALU one
+    decode_kernel = ("decode_mfma" if spec.dtype == "bf16" and pk.pa_get_option(pk.PA_OPT_DECODE_KERNEL) != 1
+                     else "decode_streamk")
     chunk_n, chunk_ms = prof["chunk_mfma"]
     decode_avg = decode_ms / decode_n if decode_n else float("nan")
     chunk_avg = chunk_ms / chunk_n if chunk_n else float("nan")
@@ -248,12 +248,13 @@ def main(argv=None):
     if use_mfma and prefill_like:
         ach = work["chunk_flops"] / (chunk_avg * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=ach, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=ach / MFMA_BF16_PEAK_TFLOPS, traffic=None, kernel="chunk_mfma",
+                    frac=ach / MFMA_BF16_PEAK_TFLOPS, traffic=recorded_traffic("chunk_mfma", spec.cfg_id),
+                    kernel="chunk_mfma", algorithmic_flops=work["chunk_flops"],
                     kernel_avg_us=chunk_avg * 1e3)
     else:
         ach = work["decode_kernel_bytes"] / (decode_avg * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS,
-                    traffic=recorded_traffic("decode_streamk", spec.cfg_id), kernel="decode_streamk",
+                    traffic=recorded_traffic(decode_kernel, spec.cfg_id), kernel=decode_kernel,
                     kernel_avg_us=decode_avg * 1e3, algorithmic_bytes=work["decode_kernel_bytes"])
         if ceil:
             roof["frac_of_measured_copy"] = ach / ceil["copy_GBps"]

@@ -30,7 +30,7 @@ PA_OPT_TARGET_ITEMS = 3
 PA_OPT_DECODE_BUFFERS = 4
 PA_OPT_DECODE_KERNEL = 5
 PA_K_RESHAPE, PA_K_PLAN, PA_K_CHUNK, PA_K_DECODE, PA_K_MERGE, PA_K_COUNT = range(6)
-KERNEL_NAMES = ["reshape_and_cache", "plan", "chunk_mfma", "decode_streamk", "split_merge"]
+KERNEL_NAMES = ["reshape_and_cache", "plan", "chunk_mfma", "decode", "split_merge"]  # PA_K_* kinds
 
 _i32, _i64, _f32, _vp, _sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
 _pi32 = C.POINTER(C.c_int32)

@@ -142,6 +142,17 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
   // DMA: in instruction j of a page, lane -> row j*RPI + lane/CH of the page,
   // LDS chunk lane%CH, which holds global chunk (lane%CH) ^ swizzle(row)
   const int dma_row = lane / CH, dma_chunk = lane % CH;
+  // so each copy instruction is a scalar page base plus these per-lane byte
+  // offsets (fixed size: an array sized by a template parameter and captured
+  // by the lambdas below is not instantiated in the host pass)
+  static_assert(IPG <= 4, "copy instructions per page");
+  uint32_t off_k[4], off_v[4];
+#pragma unroll
+  for (int j = 0; j < IPG; ++j) {
+    const int row = j * RPI + dma_row;  // token within the page
+    off_k[j] = uint32_t(row * RB + 16 * (dma_chunk ^ (row & (CH - 1))));
+    off_v[j] = uint32_t(row * RB + 16 * (dma_chunk ^ (v_swz(row) & (CH - 1))));
+  }
 
   const int n_items = w.hdr[H_TILES] * a.hkv;
   const int64_t page_stride = int64_t(kBlock) * RB;
@@ -261,14 +272,13 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
       raw = __builtin_amdgcn_readfirstlane(raw);
       const int32_t blk = raw < 0 ? 0 : (raw >= a.nb ? int32_t(a.nb - 1) : raw);  // never leave the pool
       const int64_t page = (int64_t(blk) * a.hkv + kvh) * page_stride;
+      const char* kp = kbase + page;
+      const char* vp = vbase + page;
 #pragma unroll
       for (int j = 0; j < IPG; ++j) {
-        const int row = j * RPI + dma_row;  // token within the page
-        const int64_t g_k = page + int64_t(row) * RB + 16 * (dma_chunk ^ (row & (CH - 1)));
-        const int64_t g_v = page + int64_t(row) * RB + 16 * (dma_chunk ^ (v_swz(row) & (CH - 1)));
         const int lrow = wave * kBlock + j * RPI;  // first LDS row of this instruction
-        __builtin_amdgcn_global_load_lds(kbase + g_k, (lds_void_t*)(dk + lrow * RB), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vbase + g_v, (lds_void_t*)(dv + lrow * RB), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(kp + off_k[j], (lds_void_t*)(dk + lrow * RB), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vp + off_v[j], (lds_void_t*)(dv + lrow * RB), 16, 0, 0);
       }
     };
     // after the DMA has landed: V rows of keys at or past kv_end become zeros
@@ -343,7 +353,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
       // the final division by l cancels the common factor.
       float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, fmaxf(s[0][j], s[1][j]));
+      for (int j = 1; j < 16; ++j) mx = fmaxf(fmaxf(mx, s[0][j]), s[1][j]);
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
       // wave-uniform branch (rarely taken after the first tiles); lanes whose
       // maximum did not grow scale by 1
