@@ -173,6 +173,8 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the copy/read ceiling measurement")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each replica's step from a captured HIP graph (one capture per replica)")
     ap.add_argument("--opt", action="append", default=[], metavar="NAME=VALUE",
                     help="library option before the run, e.g. DECODE_BUFFERS=1")
     args = ap.parse_args(argv)
@@ -212,9 +214,25 @@ def main(argv=None):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        graphs = []
+        for r in range(reps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+        def run(i):
+            graphs[i % reps].replay()
+
+        for i in range(args.warmup):
+            run(i)
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i)
+        run(args.warmup + i)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     # second pass with HIP-event timing around every kernel launch of the step
@@ -268,6 +286,7 @@ def main(argv=None):
                    "causal_flops": work["causal_flops"], "replicas": reps},
         "roofline": roof,
         "kernels_avg_us": {k: (v[1] / v[0] * 1e3 if v[0] else None) for k, v in prof.items()},
+        "launch": "hip_graph" if args.graph else "stream",
         "ceilings": ceil,
     }
     if not args.no_cpu_baseline:
