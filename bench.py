@@ -163,6 +163,75 @@ def cpu_baseline(spec, seconds: float):
                        f"sequences of this workload, {dt:.1f} s of host compute")
 
 
+def engine_bench(args, pk, torch):
+    """A continuous-batching run: every step of an engine loop (chunked prefill,
+    decodes, preemption by recompute, block reuse) against one persistent pool.
+    Steps are formed and their inputs staged in HBM first; the timed region runs
+    every step's scatter and attention once, after one untimed pass."""
+    import numpy as np
+
+    import workloads as W
+
+    cfg = W.EngineConfig(num_blocks=args.engine_blocks, token_budget=1024, chunk=256, max_running=128,
+                         num_requests=192, prompt_range=(1, 1024), output_range=(1, 128), arrival_span=64,
+                         num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16", seed=11)
+    eng = W.EngineLoop(cfg, pk.BlockPool(cfg.num_blocks, 16, None), table_rows=1 << 16)
+    dev = "cuda:0"
+    staged = []
+    tokens = kv_bytes = 0
+    while True:
+        st = eng.next_step()
+        if st is None:
+            break
+        spec, meta = st.spec, st.meta
+        if spec.num_tokens == 0:
+            continue
+        keys = np.concatenate([np.full(r.query, r.key) for r in spec.requests]).astype(np.int64)
+        pos = np.concatenate([np.arange(r.context, r.seq_len) for r in spec.requests]).astype(np.int64)
+        kt, pt = torch.from_numpy(keys).to(dev), torch.from_numpy(pos).to(dev)
+        q = W.value_table(spec, "q", dev)[W.q_rows(spec, kt, pt)]
+        kn = W.value_table(spec, "k", dev)[W.kv_rows(spec, "k", kt, pt)]
+        vn = W.value_table(spec, "v", dev)[W.kv_rows(spec, "v", kt, pt)]
+        i32 = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+               for a in (meta.slot_mapping, meta.block_tables, meta.seq_lens, meta.query_start_loc,
+                         meta.context_lens)]
+        out = torch.empty((spec.num_tokens, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device=dev)
+        ws = torch.empty(pk.pa_attention_workspace_size(spec.num_seqs, spec.num_tokens, spec.num_q_heads,
+                                                        spec.num_kv_heads, spec.head_dim, meta.max_blocks_per_seq),
+                         dtype=torch.uint8, device=dev)
+        staged.append((spec, q, kn, vn, i32, out, ws, max(r.query for r in spec.requests)))
+        tokens += spec.num_tokens
+        kv_bytes += sum(r.seq_len for r in spec.requests) * 2 * spec.num_kv_heads * spec.head_dim * 2
+    shape = (cfg.num_blocks, cfg.num_kv_heads, 16, cfg.head_dim)
+    kc = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+
+    def run_all():
+        for spec, q, kn, vn, (sm, bt, sl, qsl, ctx), out, ws, mq in staged:
+            pk.pa_reshape_and_cache(kn, vn, sm, kc, vc)
+            pk.pa_attention(q, kc, vc, bt, sl, qsl, ctx, spec.scale, out=out, workspace=ws, max_query_len=mq)
+
+    run_all()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_all()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    res = {
+        "metric": "engine loop: query tokens/s over a continuous-batching run", "value": tokens / dt,
+        "unit": "tokens/s", "n_gpus": 1, "steps": len(staged), "warmup": 1, "ms_per_step": dt * 1e3 / len(staged),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": (f"engine loop bf16: {cfg.num_requests} requests, prompts U[1,1024], outputs "
+                                f"U[1,128], arrivals over {cfg.arrival_span} steps, budget {cfg.token_budget} "
+                                f"tokens/step, chunks <= {cfg.chunk}, <= {cfg.max_running} running; Hq=32 Hkv=8 "
+                                f"D=128 block=16 pool={cfg.num_blocks} blocks"),
+                   "query_tokens": tokens, "preemptions": eng.preemptions},
+        "kv_read_GBps": kv_bytes / dt / 1e9,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +242,9 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the copy/read ceiling measurement")
+    ap.add_argument("--engine", action="store_true",
+                    help="time a multi-step continuous-batching run instead of one step")
+    ap.add_argument("--engine-blocks", type=int, default=2560, help="pool size of the engine run")
     ap.add_argument("--graph", action="store_true",
                     help="replay each replica's step from a captured HIP graph (one capture per replica)")
     ap.add_argument("--opt", action="append", default=[], metavar="NAME=VALUE",
@@ -194,6 +266,8 @@ def main(argv=None):
         name, val = o.split("=")
         pk.pa_set_option(getattr(pk, "PA_OPT_" + name), int(val))
     torch.cuda.set_device(0)
+    if args.engine:
+        return engine_bench(args, pk, torch)
     ceil = None if args.no_ceilings else measure_ceilings(pk, torch)
     spec = W.make_config(args.config)
     # rotate over enough replicas that the K/V read since a replica's last use

@@ -26,3 +26,4 @@ from .values import (  # noqa: F401
     poison_bits,
 )
 from .step import StepMeta, run_allocation_script, step_rows  # noqa: F401
+from .engine import EngineConfig, EngineLoop, EngineRequest, EngineStep  # noqa: F401
