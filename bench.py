@@ -35,7 +35,8 @@ def workload_desc(spec) -> str:
              2: "decode-only bf16: 64 seqs x 1 token, context U[512,2048]",
              3: "chunked-prefill bf16: 8 x 512-token chunks over context 0/512/1024/1536",
              4: "mixed bf16, 8192-token budget: 4 x 512-token chunks + 6144 decodes (context U[1024,8192])",
-             5: "long-context + prefix-shared decode bf16: 256 decodes sharing 128 blocks + 16 at 64k-128k"}
+             5: "long-context + prefix-shared decode bf16: 256 decodes sharing 128 blocks + 16 at 64k-128k",
+             6: "short-query verify bf16: 64 seqs x 4 query tokens, context U[512,2048]"}
     return (f"{kinds.get(spec.cfg_id, spec.name)}; Hq={spec.num_q_heads} Hkv={spec.num_kv_heads} "
             f"D={spec.head_dim} block=16 pool={spec.num_blocks} blocks")
 
@@ -46,16 +47,17 @@ def _unique_tokens(spec, reqs):
     return sum(r.seq_len for r in reqs) - spec.prefix_tokens * max(0, sharers - 1)
 
 
-def algorithmic_work(spec, mfma_rows: bool):
+def algorithmic_work(spec, mfma_rows: bool, verify_rows: int = 1):
     """Bytes and FLOPs the method itself must move / compute in one step.
 
     K/V bytes count each physical token once per step (kv heads read once, not per
     query head); causal FLOPs count only unmasked (query, key) pairs, 2 for QK^T and
-    2 for PV per pair per query head."""
+    2 for PV per pair per query head.  Short queries (2..verify_rows rows) go row-wise."""
     elt, hkv, hq, d = spec.elt_bytes, spec.num_kv_heads, spec.num_q_heads, spec.head_dim
     kv_tok = 2 * hkv * d * elt
-    row_reqs = [r for r in spec.requests if r.query == 1 or (r.query > 1 and not mfma_rows)]
-    chunk_reqs = [r for r in spec.requests if r.query > 1 and mfma_rows]
+    row_reqs = [r for r in spec.requests
+                if r.query == 1 or (r.query > 1 and (not mfma_rows or r.query <= verify_rows))]
+    chunk_reqs = [r for r in spec.requests if r.query > verify_rows and r.query > 1 and mfma_rows]
     pair_flops = lambda r: 4 * d * hq * (r.query * r.context + r.query * (r.query + 1) // 2)
     rows = sum(r.query for r in row_reqs)
     decode_bytes = (_unique_tokens(spec, row_reqs) * kv_tok + rows * hq * d * (elt + 4)
@@ -237,7 +239,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--replicas", type=int, default=0, help="input replicas to rotate over (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -320,7 +322,11 @@ def main(argv=None):
     pk.pa_profile_enable(0)
 
     use_mfma = spec.dtype == "bf16" and pk.pa_get_option(pk.PA_OPT_FORCE_ROWWISE) == 0 and prof["chunk_mfma"][0] > 0
-    work = algorithmic_work(spec, use_mfma)
+    g = spec.num_q_heads // spec.num_kv_heads
+    vr_opt = pk.pa_get_option(pk.PA_OPT_VERIFY_ROWS)
+    verify = (1 if spec.dtype != "bf16" or pk.pa_get_option(pk.PA_OPT_DECODE_KERNEL) == 1
+              or pk.pa_get_option(pk.PA_OPT_FORCE_ROWWISE) else min(vr_opt or 16 // g, 16 // g))
+    work = algorithmic_work(spec, use_mfma, verify)
     ms = dt * 1e3 / args.steps
     decode_n, decode_ms = prof["decode"]
     # the row-wise kernel bf16 steps take unless an option picks the VALU one

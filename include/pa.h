@@ -148,8 +148,13 @@ enum {
   PA_OPT_DECODE_BUFFERS = 4, /* 1 or 2: pages in registers per wavefront of the VALU row-wise
                                 kernel (2 = the next page's loads overlap this page's math);
                                 0: automatic */
-  PA_OPT_DECODE_KERNEL = 5   /* row-wise rows of bf16 steps: 0 automatic (MFMA), 1 VALU kernel,
+  PA_OPT_DECODE_KERNEL = 5,  /* row-wise rows of bf16 steps: 0 automatic (MFMA), 1 VALU kernel,
                                 2 MFMA kernel; float32 steps always take the VALU kernel */
+  PA_OPT_VERIFY_ROWS = 6     /* bf16 steps with the MFMA row-wise kernel: a sequence with 2..n
+                                query rows (a short query, e.g. speculative-decoding verification)
+                                is one row-wise work item whose rows share every K/V page instead
+                                of chunk tiles; n = this value capped at 16 / (q heads per kv
+                                head); 0 (automatic) and 1: off.  Changes the workspace size */
 };
 int pa_set_option(int32_t option, int64_t value);
 int64_t pa_get_option(int32_t option);

@@ -95,6 +95,15 @@ int64_t ranges_capacity(const StepShape& s) {
   return cap;
 }
 
+int verify_rows(int group) {
+  const int cap = 16 / (group > 0 && group <= 16 ? group : 16);  // one 16-wide accumulator
+  const int64_t v = option(PA_OPT_VERIFY_ROWS);
+  // automatic: off -- the chunk kernel measured faster on short queries
+  // (64 sequences x 2..4 rows over contexts of 512-2048: 86-89 us against 92-99 us)
+  if (v >= 1) return v < cap ? int(v) : cap;
+  return 1;
+}
+
 Workspace layout_workspace(const StepShape& s, void* ws) {
   Workspace w{};
   const int64_t T = s.num_tokens > 0 ? s.num_tokens : 1;
@@ -102,6 +111,7 @@ Workspace layout_workspace(const StepShape& s, void* ws) {
   w.rows_cap = T;
   w.tiles_cap = T;
   w.ranges_cap = ranges_capacity(s);
+  w.ncol = int32_t(G * verify_rows(int(G)));
   char* p = static_cast<char*>(ws);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -117,8 +127,8 @@ Workspace layout_workspace(const StepShape& s, void* ws) {
   w.tiles_tmp = reinterpret_cast<int4*>(take(w.tiles_cap * sizeof(int4)));
   w.range_row = reinterpret_cast<int32_t*>(take(w.ranges_cap * sizeof(int32_t)));
   w.range_cut = reinterpret_cast<int2*>(take(w.ranges_cap * sizeof(int2)));
-  w.part_o = reinterpret_cast<float*>(take(size_t(2 * w.ranges_cap * G) * s.head_dim * sizeof(float)));
-  w.part_ml = reinterpret_cast<float2*>(take(size_t(2 * w.ranges_cap * G) * sizeof(float2)));
+  w.part_o = reinterpret_cast<float*>(take(size_t(2 * w.ranges_cap * w.ncol) * s.head_dim * sizeof(float)));
+  w.part_ml = reinterpret_cast<float2*>(take(size_t(2 * w.ranges_cap * w.ncol) * sizeof(float2)));
   w.bytes = off;
   return w;
 }
@@ -212,6 +222,10 @@ extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_ca
     pa_args.num_ranges = int32_t(n < 1 ? 1 : n);
   }
   pa_args.tile_rows = use_mfma ? chunk_tile_rows(group) : 1;
+  // short queries share their pages in one record: only the MFMA decode kernel
+  // has the per-column causal limits (and the debug route keeps one row per record)
+  pa_args.verify_rows =
+      bf16 && max_query_len > 1 && decode_uses_mfma(1) && !option(PA_OPT_FORCE_ROWWISE) ? verify_rows(group) : 1;
 
   AttnArgs a{};
   a.q = q;
@@ -231,6 +245,7 @@ extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_ca
   a.mbps = max_blocks_per_seq;
   a.nb = num_blocks;
   a.bf16 = bf16 ? 1 : 0;
+  a.merge_rows = pa_args.verify_rows;
 
   hipError_t e;
   {

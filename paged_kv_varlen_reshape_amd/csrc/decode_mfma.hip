@@ -10,6 +10,10 @@
 // normalised output for whole (row, kv head) segments and (o, max, sum)
 // partials for segments a range boundary cuts (split_merge folds them).
 //
+// A record is one decode row, or the nq <= 16 / G rows of a short query
+// (speculative-decoding verification): its rows share every K/V page and
+// accumulator column c is row c / G, head c % G, with that row's causal limit.
+//
 // Per 16-token page of one kv head, with the GQA group's G query heads:
 //   S^T[key][head] = K Q^T  on v_mfma_f32_16x16x32_bf16 (A = K straight from
 //     the pool into registers: lane l holds key l%16, dims 8*(l/16) + 32kk;
@@ -105,9 +109,11 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int gwave = blockIdx.x * kWaves + wave;
   const int nwaves = gridDim.x * kWaves;
-  const int hq = lane & 15;   // accumulator column: query head within the group
+  // accumulator column: query row hq / G of the record, head hq % G of the group
+  // (a decode record has one row; a short query's record has up to 16 / G)
+  const int hq = lane & 15;
   const int grp = lane >> 4;  // lane group: keys 4grp..4grp+3 of a page in S
-  const bool head_ok = hq < G;
+  const int jrow = hq / G, hh = hq - (hq / G) * G;
 
   // V^T operand addresses of this lane (transposed reads, see the header)
   int vaddr[DB];
@@ -139,17 +145,19 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
     bool first = true;
 
     while (x < x_end) {
-      const int tok = rec.x, seq = rec.y, len = rec.z;
+      const int tok = rec.x, seq = rec.y, len = rec.z, nq = rec.w;
+      const bool col_ok = jrow < nq;
+      const int lim = len - nq + 1 + jrow;  // keys this column's row sees
       const int n = int(min(int64_t(pages - p0), x_end - x));  // pages of this segment
       const int32_t* btrow = a.bt + int64_t(seq) * a.mbps + p0;
 
-      // Q as the B operand: head hq (zeros past G), dims 8*grp + 32kk
+      // Q as the B operand: row jrow, head hh (zeros past the record), dims 8*grp + 32kk
       u32x4 qf[KS];
       {
-        const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) +
-                                                         (int64_t(tok) * a.hq + int64_t(kvh) * G + hq) * RB);
+        const u32x4* qp = reinterpret_cast<const u32x4*>(
+            static_cast<const char*>(a.q) + (int64_t(tok + (col_ok ? jrow : 0)) * a.hq + int64_t(kvh) * G + hh) * RB);
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) qf[kk] = head_ok ? qp[grp + 4 * kk] : u32x4{0u, 0u, 0u, 0u};
+        for (int kk = 0; kk < KS; ++kk) qf[kk] = col_ok ? qp[grp + 4 * kk] : u32x4{0u, 0u, 0u, 0u};
       }
 
       f32x4_t o[DB];
@@ -188,7 +196,7 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
         char* vs = (decltype(bufc)::value ? s_v1 : s_v0)[wave];
         const int pos0 = (p0 + j) * kBlock;  // first key of the page
         if (pos0 + kBlock > len) {
-          // last, partly filled page: its V rows past the row must not reach PV
+          // last, partly filled page: its V rows past the last row must not reach PV
           for (int idx = lane; idx < kBlock * CH; idx += kWave)
             if (pos0 + idx / CH >= len) *reinterpret_cast<u32x4*>(vs + idx * 16) = u32x4{0u, 0u, 0u, 0u};
         }
@@ -199,7 +207,7 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
                                                      __builtin_bit_cast(bf16x8_t, qf[kk]), s, 0, 0, 0);
         const int kfirst = pos0 + 4 * grp;  // key of accumulator row 0 of this lane
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] = kfirst + i < len ? s[i] * a.scale_log2 : -INFINITY;
+        for (int i = 0; i < 4; ++i) s[i] = kfirst + i < lim ? s[i] * a.scale_log2 : -INFINITY;
         float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -251,20 +259,20 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
       // accumulator row i of block db is dim 16db + 4grp + i
       const bool whole = p0 == 0 && n == pages;
       const int64_t slot = int64_t(g) * 2 + (first ? 0 : 1);
-      if (head_ok) {
+      if (col_ok) {
         if (whole) {
           const float inv = 1.f / l;
-          float* op = a.out + (int64_t(tok) * a.hq + int64_t(kvh) * G + hq) * D + 4 * grp;
+          float* op = a.out + (int64_t(tok + jrow) * a.hq + int64_t(kvh) * G + hh) * D + 4 * grp;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
             *reinterpret_cast<float4*>(op + 16 * db) =
                 make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
         } else {
-          float* po = w.part_o + (slot * G + hq) * D + 4 * grp;
+          float* po = w.part_o + (slot * w.ncol + hq) * D + 4 * grp;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
             *reinterpret_cast<float4*>(po + 16 * db) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
-          if (grp == 0) w.part_ml[slot * G + hq] = make_float2(m, l);
+          if (grp == 0) w.part_ml[slot * w.ncol + hq] = make_float2(m, l);
         }
       }
 
@@ -330,7 +338,16 @@ hipError_t launch_d(const AttnArgs& a, const Workspace& w, int group, hipStream_
 
 }  // namespace
 
-int decode_mfma_waves(int head_dim, int group) { return head_dim == 64 ? waves_d<64>(group) : waves_d<128>(group); }
+// Decode ranges of a step by default: one workgroup's wavefronts per CU.  Every
+// CU then streams the same share, and fewer wavefronts per CU measured faster
+// than the three workgroups that fit (configuration 2: 63 vs 70 us; range
+// counts that are not a multiple of the CU count leave some CUs a second
+// workgroup, whose share then sets the tail).
+int decode_mfma_waves(int head_dim, int group) {
+  const int resident = head_dim == 64 ? waves_d<64>(group) : waves_d<128>(group);
+  const int one_per_cu = device_cus() * kWaves;
+  return one_per_cu < resident ? one_per_cu : resident;
+}
 
 hipError_t launch_decode_mfma(const AttnArgs& a, const Workspace& w, int group, hipStream_t st) {
   return a.d == 64 ? launch_d<64>(a, w, group, st) : launch_d<128>(a, w, group, st);

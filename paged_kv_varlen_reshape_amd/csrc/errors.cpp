@@ -14,6 +14,7 @@ std::atomic<int64_t> g_split_tokens{0};
 std::atomic<int64_t> g_target_items{0};
 std::atomic<int64_t> g_decode_buffers{0};
 std::atomic<int64_t> g_decode_kernel{0};
+std::atomic<int64_t> g_verify_rows{0};
 }  // namespace
 
 int fail(int code, const char* fmt, ...) {
@@ -35,6 +36,7 @@ int64_t option(int32_t id) {
     case PA_OPT_TARGET_ITEMS: return g_target_items.load();
     case PA_OPT_DECODE_BUFFERS: return g_decode_buffers.load();
     case PA_OPT_DECODE_KERNEL: return g_decode_kernel.load();
+    case PA_OPT_VERIFY_ROWS: return g_verify_rows.load();
     default: return -1;
   }
 }
@@ -64,6 +66,10 @@ extern "C" int pa_set_option(int32_t id, int64_t value) {
     case PA_OPT_DECODE_KERNEL:
       if (value < 0 || value > 2) return pa::fail(PA_ERR_INVALID, "PA_OPT_DECODE_KERNEL takes 0, 1 or 2");
       pa::g_decode_kernel = value;
+      return PA_OK;
+    case PA_OPT_VERIFY_ROWS:
+      if (value < 0 || value > 16) return pa::fail(PA_ERR_INVALID, "PA_OPT_VERIFY_ROWS takes 0..16");
+      pa::g_verify_rows = value;
       return PA_OK;
     default:
       return pa::fail(PA_ERR_INVALID, "unknown option %d", id);

@@ -44,16 +44,19 @@ enum PlanHeader : int {
 struct Workspace {
   int64_t* hdr64;      // hdr + H64
   int32_t* hdr;        // [H_WORDS]
-  int4* rows;          // [rows_cap]   {token row, seq, keys seen, 0}
+  int4* rows;          // [rows_cap]   {first token row, seq, keys seen by its last row, query rows nq}:
+                       //   nq consecutive rows of one sequence (nq > 1: a short query whose
+                       //   rows share every K/V page, one accumulator column per row and head)
   int64_t* rows_base;  // [rows_cap]   first unit of each row
   int2* tiles;         // [tiles_cap]  {seq, first query row of the tile within the sequence},
                        //   longest first
   int4* tiles_tmp;     // [tiles_cap]  plan scratch: tiles in sequence order with their bucket
   int32_t* range_row;  // [ranges_cap] row holding each range's first unit
   int2* range_cut;     // [ranges_cap] {row, kv head} first cut by this range's start, or {-1, -1}
-  float* part_o;       // [2 * ranges_cap * G * D] unnormalised partial outputs
-  float2* part_ml;     // [2 * ranges_cap * G]     partial (max, sum), log2 domain
+  float* part_o;       // [2 * ranges_cap * ncol * D] unnormalised partial outputs
+  float2* part_ml;     // [2 * ranges_cap * ncol]     partial (max, sum), log2 domain
   int64_t rows_cap, tiles_cap, ranges_cap;
+  int32_t ncol;        // columns per partial slot: G * (most query rows of one record)
   size_t bytes;
 };
 
@@ -63,6 +66,8 @@ struct StepShape {
 
 // Decode ranges the workspace must hold for this shape.
 int64_t ranges_capacity(const StepShape& s);
+// Most query rows one row-wise record may hold for this group size (option, else 16 / group).
+int verify_rows(int group);
 
 // Carve the workspace (ws == nullptr: only compute sizes).
 Workspace layout_workspace(const StepShape& s, void* ws);
@@ -83,6 +88,8 @@ struct PlanArgs {
   int32_t fixed_units;    // >0: units per decode range
   int32_t num_ranges;     // automatic: spread the units over this many ranges
   int32_t tile_rows;      // query rows per chunk-kernel tile
+  int32_t verify_rows;    // >1: sequences with 2..verify_rows query rows become one row-wise
+                          //   record (their rows share the K/V pages); 1: one record per row
 };
 hipError_t launch_plan(const PlanArgs& a, const Workspace& w, hipStream_t st);
 
@@ -99,6 +106,7 @@ struct AttnArgs {
   int32_t num_seqs, num_tokens, hq, hkv, d, mbps;
   int64_t nb;
   int32_t bf16;
+  int32_t merge_rows;  // most query rows of one row-wise record this step (the plan's verify_rows)
 };
 hipError_t launch_decode(const AttnArgs& a, const Workspace& w, int group, hipStream_t st);
 // Resident decode wavefronts on the current device for this kernel instance.

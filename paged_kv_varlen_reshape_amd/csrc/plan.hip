@@ -6,7 +6,9 @@
 // decodes (section "エンジンの中核：スケジューラとKVキャッシュ管理").  Each
 // sequence's query rows go either to the MFMA chunk kernel (bf16 sequences
 // with more than one query row, in tiles of `tile_rows` rows) or to the
-// row-wise decode kernel (decodes, and every row when MFMA is off).  A
+// row-wise decode kernel (decodes, and every row when MFMA is off).  A short
+// query (2..verify_rows rows, as in speculative-decoding verification) is one
+// row-wise record whose rows share every page of its last row.  A
 // row-wise row at absolute position p sees p+1 keys, i.e. ceil((p+1)/16)
 // pages per kv head; all those (row, kv head, page) units form one stream
 // that is cut into equal ranges, one per decode wavefront.
@@ -70,7 +72,8 @@ __device__ __forceinline__ int64_t pages_upto(int64_t n) {
 
 struct SeqInfo {
   int32_t r0, q, c;
-  bool chunk;
+  bool chunk;   // query rows go to the chunk kernel in tiles
+  bool group;   // query rows form one row-wise record (a short query)
 };
 
 // Sequence i's rows, clamped so that nothing below indexes outside the
@@ -86,13 +89,17 @@ __device__ __forceinline__ SeqInfo seq_info(const PlanArgs& a, int64_t i, bool v
   if (!valid || r0 < 0 || r0 >= a.num_tokens) q = 0;
   c = max(c, 0);
   if (int64_t(c) + q > a.max_len) q = c >= a.max_len ? 0 : a.max_len - c;
-  return SeqInfo{r0, q, c, q > 1 && a.use_mfma};
+  const bool group = q > 1 && q <= a.verify_rows;
+  return SeqInfo{r0, q, c, !group && q > 1 && a.use_mfma, group};
 }
 
 __device__ __forceinline__ void seq_counts(const SeqInfo& s, int tile_rows, int64_t hkv, int64_t& ntile,
                                            int64_t& nrow, int64_t& nunit) {
   if (s.chunk) {
     ntile += (s.q + tile_rows - 1) / tile_rows;
+  } else if (s.group) {
+    nrow += 1;
+    nunit += hkv * ((int64_t(s.c) + s.q + kBlock - 1) / kBlock);  // the pages of its last row
   } else if (s.q > 0) {
     nrow += s.q;
     nunit += hkv * (pages_upto(int64_t(s.c) + s.q) - pages_upto(s.c));
@@ -136,10 +143,12 @@ plan_kernel(PlanArgs a, Workspace w) {
             w.tiles_tmp[t] = make_int4(int(ib + c), first, int32_t(bucket < kSortBuckets ? bucket : kSortBuckets - 1), 0);
           }
         } else {
-          for (int32_t j = 0; j < s.q && r < w.rows_cap; ++j, ++r) {
-            const int32_t len = s.c + j + 1;
+          // one record per row, or one for all rows of a short query
+          const int32_t nrec = s.group ? 1 : s.q, nq = s.group ? s.q : 1;
+          for (int32_t j = 0; j < nrec && r < w.rows_cap; ++j, ++r) {
+            const int32_t len = s.c + j + nq;  // keys seen by the record's last row
             const int32_t pages = (len + kBlock - 1) / kBlock;
-            w.rows[r] = make_int4(s.r0 + j, int(ib + c), len, 0);
+            w.rows[r] = make_int4(s.r0 + j, int(ib + c), len, nq);
             w.rows_base[r] = u;
             if (r < kLdsRows) {
               s_base[r] = u;

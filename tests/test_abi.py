@@ -102,7 +102,7 @@ def test_workspace_size_is_deterministic_and_grows():
 
 def test_options_roundtrip_and_errors():
     for opt, val in ((pk.PA_OPT_FORCE_ROWWISE, 1), (pk.PA_OPT_SPLIT_TOKENS, 64), (pk.PA_OPT_TARGET_ITEMS, 100),
-                     (pk.PA_OPT_DECODE_BUFFERS, 2), (pk.PA_OPT_DECODE_KERNEL, 1)):
+                     (pk.PA_OPT_DECODE_BUFFERS, 2), (pk.PA_OPT_DECODE_KERNEL, 1), (pk.PA_OPT_VERIFY_ROWS, 3)):
         old = pk.pa_get_option(opt)
         pk.pa_set_option(opt, val)
         assert pk.pa_get_option(opt) == val
@@ -115,5 +115,7 @@ def test_options_roundtrip_and_errors():
         pk.pa_set_option(pk.PA_OPT_DECODE_BUFFERS, 3)
     with pytest.raises(pk.PAError):
         pk.pa_set_option(pk.PA_OPT_DECODE_KERNEL, -1)
+    with pytest.raises(pk.PAError):
+        pk.pa_set_option(pk.PA_OPT_VERIFY_ROWS, 17)
     with pytest.raises(pk.PAError):
         pk.pa_set_option(99, 0)

@@ -44,6 +44,7 @@ def _reset_options():
     pk.pa_set_option(pk.PA_OPT_TARGET_ITEMS, 0)
     pk.pa_set_option(pk.PA_OPT_DECODE_BUFFERS, 0)
     pk.pa_set_option(pk.PA_OPT_DECODE_KERNEL, 0)
+    pk.pa_set_option(pk.PA_OPT_VERIFY_ROWS, 0)
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3])
@@ -74,7 +75,7 @@ def test_reshape_skips_negative_slots_and_empty_call():
     pk.pa_reshape_and_cache(ds.k_new[:0], ds.v_new[:0], sm[:0], ds.k_cache, ds.v_cache)
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 6])
 def test_attention_matches_oracle_every_row(cfg):
     spec = W.make_config(cfg)
     print(f"attention parity cfg{cfg}", flush=True)
@@ -140,6 +141,28 @@ def test_many_sequences_plan_fallbacks():
     for split in (0, 16):
         pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, split)
         _check_attention(spec, ds, ds.attention(), seqs)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_short_queries_share_pages(seed):
+    """Sequences with 2..16/G query rows as one row-wise record (their rows share every
+    page, one MFMA column per row and head) against the oracle; with the grouping off
+    (chunk kernel), capped at 3 rows, and with range lengths that cut the records."""
+    r = np.random.default_rng(seed)
+    g = [1, 2, 4, 8][seed % 4]
+    hkv = [2, 1][(seed // 4) % 2]
+    d = [64, 128][(seed // 2) % 2]
+    spec = W.random_spec(200 + seed, num_seqs=int(r.integers(4, 12)), max_context=int(r.integers(20, 400)),
+                         max_query=8, num_q_heads=hkv * g, num_kv_heads=hkv, head_dim=d, dtype="bf16",
+                         prefix_tokens=16, decode_fraction=0.3)
+    print(f"short queries seed={seed} g={g} hkv={hkv} d={d} q={[x.query for x in spec.requests]}", flush=True)
+    ds = build_device_step(spec)
+    ds.reshape()
+    for vr in (16, 1, 3):  # the cap 16 / G, off (chunk kernel), at most 3 rows
+        pk.pa_set_option(pk.PA_OPT_VERIFY_ROWS, vr)
+        for split in (0, 16, 48):
+            pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, split)
+            _check_attention(spec, ds, ds.attention())
 
 
 def test_max_query_len_hint_never_changes_results():

@@ -15,7 +15,7 @@ def test_cpp_pool_meets_the_pins(pin):
     pin(pk.BlockPool)
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
 def test_cpp_pool_equals_reference_on_configs(cfg):
     spec = W.make_config(cfg)
     a, b = pk.BlockPool(spec.num_blocks, 16, spec.initial_order), RefBlockPool(spec.num_blocks, 16, spec.initial_order)

@@ -30,6 +30,7 @@ CONFIG_NAMES = {
     3: "chunked_prefill_bf16",
     4: "mixed_8192_bf16",
     5: "long_prefix_bf16",
+    6: "verify_bf16",  # an extra workload, not one of the five measured configurations
 }
 
 
@@ -96,7 +97,8 @@ def _blocks(tokens: int, bs: int = 16) -> int:
 
 
 def make_config(cfg_id: int) -> StepSpec:
-    """Return the seeded spec of step configuration ``cfg_id`` (1..5)."""
+    """Return the seeded spec of step configuration ``cfg_id`` (1..5; 6 is an extra
+    short-query workload)."""
     rng = np.random.default_rng((cfg_id, 1))
     if cfg_id == 1:
         # a 17-token fresh prefill (2 blocks) and two 1-token decodes over 5 and 33 cached tokens
@@ -135,6 +137,13 @@ def make_config(cfg_id: int) -> StepSpec:
             nb += _blocks(r.seq_len) - (_blocks(prefix) if r.shares_prefix else 0)
         return StepSpec(CONFIG_NAMES[5], 5, 64, 8, 128, "bf16", 16, nb, 1.0 / math.sqrt(128), reqs,
                         prefix_tokens=prefix, initial_order=_order(5, nb), table_rows=1 << 18, seed=5)
+    if cfg_id == 6:
+        # speculative-decoding verification: each of 64 sequences checks 4 drafted tokens
+        ctx = rng.integers(512, 2048, size=64, endpoint=True)
+        reqs = [Request(i, int(c), 4) for i, c in enumerate(ctx)]
+        nb = 16384
+        return StepSpec(CONFIG_NAMES[6], 6, 32, 8, 128, "bf16", 16, nb, 1.0 / math.sqrt(128), reqs,
+                        initial_order=_order(6, nb), table_rows=1 << 16, seed=6)
     raise ValueError(f"unknown config id {cfg_id}")
 
 
