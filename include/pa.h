@@ -144,10 +144,11 @@ enum {
                                 (row, kv head) pages (multiple of 16); 0: automatic, the step's
                                 pages spread evenly over the resident wavefronts */
   PA_OPT_TARGET_ITEMS = 3,   /* >0: number of decode ranges in automatic mode; 0: one per
-                                resident decode wavefront */
-  PA_OPT_DECODE_BUFFERS = 4, /* 1 or 2: pages in registers per wavefront of the VALU row-wise
-                                kernel (2 = the next page's loads overlap this page's math);
-                                0: automatic */
+                                resident wavefront (VALU kernel) or per wavefront of one
+                                workgroup per CU (MFMA kernel) */
+  PA_OPT_DECODE_BUFFERS = 4, /* pages a decode wavefront holds at once (the page being scored
+                                plus the ones in flight): VALU kernel 1 or 2, MFMA kernel 2..4;
+                                0 or a value the kernel does not take: automatic */
   PA_OPT_DECODE_KERNEL = 5,  /* row-wise rows of bf16 steps: 0 automatic (MFMA), 1 VALU kernel,
                                 2 MFMA kernel; float32 steps always take the VALU kernel */
   PA_OPT_VERIFY_ROWS = 6     /* bf16 steps with the MFMA row-wise kernel: a sequence with 2..n

@@ -30,9 +30,10 @@
 //     V[4g + 0..3][16dblk + i] for its lane group g).
 // The page's 16-byte chunks are XOR-swizzled by row (2*(row%4) + 8*(row/4%2))
 // so the transposed loads touch distinct banks; the DMA picks, per lane, the
-// global chunk that belongs in its LDS slot.  Two LDS page buffers per
-// wavefront (separate arrays, named at compile time) let the next page's K
-// loads and V DMA fly while the current page is multiplied, with no barrier.
+// global chunk that belongs in its LDS slot.  NBUF LDS page buffers per
+// wavefront (separate arrays, named at compile time) let the next NBUF - 1
+// pages' K loads and V DMA fly while the current page is multiplied, with no
+// barrier.
 //
 // Softmax in fp32 in the log2 domain; P is rounded to bf16 for the PV product
 // and l sums the rounded weights, so each output is an exact convex
@@ -56,8 +57,8 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-using B0 = std::integral_constant<int, 0>;
-using B1 = std::integral_constant<int, 1>;
+template <int B>
+using Buf = std::integral_constant<int, B>;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
@@ -89,25 +90,34 @@ __device__ __forceinline__ int v_swz(int row) {
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their maxima)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(N | (7 << 4) | (15 << 8));
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D, int G>
-__global__ void __launch_bounds__(kThreads, 3)
+template <int D, int G, int NBUF>
+__global__ void __launch_bounds__(kThreads, 2)
 decode_mfma_kernel(AttnArgs a, Workspace w) {
   using C = DecM<D>;
   constexpr int RB = C::RB, CH = C::CH, RPI = C::RPI, IPG = C::IPG, KS = C::KS, DB = C::DB, PAGE = C::PAGE;
   static_assert(G <= 16, "one 16-wide accumulator column per head");
+  static_assert(NBUF >= 2 && NBUF <= 4, "page buffers per wavefront");
+  constexpr int PER_PAGE = IPG + KS;  // vector memory operations issued per page
 
-  // two page buffers per wavefront, separate arrays so that the compiler sees
-  // the DMA in flight does not write what is being read
+  // NBUF page buffers per wavefront (page j in buffer j % NBUF), separate
+  // arrays so that the compiler sees the DMA in flight does not write what is
+  // being read
   __shared__ __attribute__((aligned(16))) char s_v0[kWaves][PAGE];
   __shared__ __attribute__((aligned(16))) char s_v1[kWaves][PAGE];
+  __shared__ __attribute__((aligned(16))) char s_v2[NBUF > 2 ? kWaves : 1][NBUF > 2 ? PAGE : 16];
+  __shared__ __attribute__((aligned(16))) char s_v3[NBUF > 3 ? kWaves : 1][NBUF > 3 ? PAGE : 16];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int gwave = blockIdx.x * kWaves + wave;
+  auto vbuf = [&](auto bufc) __attribute__((always_inline)) -> char* {
+    constexpr int B = decltype(bufc)::value;
+    return B == 0 ? s_v0[wave] : B == 1 ? s_v1[wave] : B == 2 ? s_v2[wave] : s_v3[wave];
+  };
   const int nwaves = gridDim.x * kWaves;
   // accumulator column: query row hq / G of the record, head hq % G of the group
   // (a decode record has one row; a short query's record has up to 16 / G)
@@ -180,7 +190,7 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
       auto issue = [&](int j, u32x4 (&kf)[KS], auto bufc) {
         if (j > 0 && (j & (kWave - 1)) == 0) load_ids(j);
         const int64_t pb = page_base(j);
-        char* dv = (decltype(bufc)::value ? s_v1 : s_v0)[wave];
+        char* dv = vbuf(bufc);
 #pragma unroll
         for (int ii = 0; ii < IPG; ++ii) {
           const int row = ii * RPI + dma_row;
@@ -193,7 +203,7 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
       };
       // one page: scores, online softmax, PV
       auto compute = [&](int j, const u32x4 (&kf)[KS], auto bufc) {
-        char* vs = (decltype(bufc)::value ? s_v1 : s_v0)[wave];
+        char* vs = vbuf(bufc);
         const int pos0 = (p0 + j) * kBlock;  // first key of the page
         if (pos0 + kBlock > len) {
           // last, partly filled page: its V rows past the last row must not reach PV
@@ -231,26 +241,35 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
         }
       };
 
+      // pages j+1 .. j+NBUF-1 fly while page j is multiplied: page j uses
+      // buffer j % NBUF and K register set j % NBUF (static in the unrolled loop)
       load_ids(0);
-      u32x4 ka[KS], kb[KS];
-      issue(0, ka, B0{});
-      for (int j = 0; j < n; j += 2) {
-        // page j+1 flies while page j is multiplied
-        if (j + 1 < n) {
-          issue(j + 1, kb, B1{});
-          wait_vmcnt<IPG + KS>();  // page j's V DMA and K loads have landed
-        } else {
-          wait_vmcnt<0>();
-        }
-        compute(j, ka, B0{});
-        if (j + 1 >= n) break;
-        if (j + 2 < n) {
-          issue(j + 2, ka, B0{});
-          wait_vmcnt<IPG + KS>();
-        } else {
-          wait_vmcnt<0>();
-        }
-        compute(j + 1, kb, B1{});
+      u32x4 kset[NBUF][KS];
+      issue(0, kset[0], Buf<0>{});
+      if constexpr (NBUF > 2) {
+        if (1 < n) issue(1, kset[1], Buf<1>{});
+      }
+      if constexpr (NBUF > 3) {
+        if (2 < n) issue(2, kset[2], Buf<2>{});
+      }
+      auto step = [&](int j, auto bufc) __attribute__((always_inline)) {
+        constexpr int B = decltype(bufc)::value;
+        constexpr int BN = (B + NBUF - 1) % NBUF;  // buffer of page j + NBUF - 1
+        if (j >= n) return;
+        if (j + NBUF - 1 < n) issue(j + NBUF - 1, kset[BN], Buf<BN>{});
+        // page j's V copy and K loads have landed; the pages issued after it may fly
+        const int later = min(NBUF - 1, n - 1 - j);
+        if (later >= 3) wait_vmcnt<3 * PER_PAGE>();
+        else if (later == 2) wait_vmcnt<2 * PER_PAGE>();
+        else if (later == 1) wait_vmcnt<PER_PAGE>();
+        else wait_vmcnt<0>();
+        compute(j, kset[B], bufc);
+      };
+      for (int j0 = 0; j0 < n; j0 += NBUF) {
+        step(j0, Buf<0>{});
+        step(j0 + 1, Buf<1>{});
+        if constexpr (NBUF > 2) step(j0 + 2, Buf<2>{});
+        if constexpr (NBUF > 3) step(j0 + 3, Buf<3>{});
       }
 
       // the four lane groups hold disjoint keys of each head
@@ -291,12 +310,13 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
   }
 }
 
-template <int D, int G>
+template <int D, int G, int NBUF>
 int resident_waves_t() {
   static int per_cu = 0;  // resident workgroups per CU, from the occupancy calculator
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<D, G>, kThreads, 0) != hipSuccess || n <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<D, G, NBUF>, kThreads, 0) != hipSuccess ||
+        n <= 0)
       n = 1;
     per_cu = n;
   }
@@ -305,22 +325,48 @@ int resident_waves_t() {
   return waves < cap ? waves : cap;
 }
 
-template <int D, int G>
+template <int D, int G, int NBUF>
 hipError_t launch_t(const AttnArgs& a, const Workspace& w, hipStream_t st) {
-  int64_t waves = resident_waves_t<D, G>();
+  int64_t waves = resident_waves_t<D, G, NBUF>();
   if (waves > w.ranges_cap) waves = w.ranges_cap;
   const int64_t grid = (waves + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL((decode_mfma_kernel<D, G>), dim3(unsigned(grid)), dim3(kThreads), 0, st, a, w);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, G, NBUF>), dim3(unsigned(grid)), dim3(kThreads), 0, st, a, w);
   return hipGetLastError();
+}
+
+// page buffers per wavefront: the option when it names 2..4, else 2 (three and
+// four measured no faster on the decode-only and long-context steps, with
+// 18 / 38 more registers)
+int mfma_buffers() {
+  const int64_t v = option(PA_OPT_DECODE_BUFFERS);
+  return v >= 2 && v <= 4 ? int(v) : 2;
+}
+
+template <int D, int G>
+int waves_g() {
+  switch (mfma_buffers()) {
+    case 4: return resident_waves_t<D, G, 4>();
+    case 3: return resident_waves_t<D, G, 3>();
+    default: return resident_waves_t<D, G, 2>();
+  }
+}
+
+template <int D, int G>
+hipError_t launch_g(const AttnArgs& a, const Workspace& w, hipStream_t st) {
+  switch (mfma_buffers()) {
+    case 4: return launch_t<D, G, 4>(a, w, st);
+    case 3: return launch_t<D, G, 3>(a, w, st);
+    default: return launch_t<D, G, 2>(a, w, st);
+  }
 }
 
 template <int D>
 int waves_d(int group) {
   switch (group) {
-    case 1: return resident_waves_t<D, 1>();
-    case 2: return resident_waves_t<D, 2>();
-    case 4: return resident_waves_t<D, 4>();
-    case 8: return resident_waves_t<D, 8>();
+    case 1: return waves_g<D, 1>();
+    case 2: return waves_g<D, 2>();
+    case 4: return waves_g<D, 4>();
+    case 8: return waves_g<D, 8>();
     default: return 1;
   }
 }
@@ -328,10 +374,10 @@ int waves_d(int group) {
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const Workspace& w, int group, hipStream_t st) {
   switch (group) {
-    case 1: return launch_t<D, 1>(a, w, st);
-    case 2: return launch_t<D, 2>(a, w, st);
-    case 4: return launch_t<D, 4>(a, w, st);
-    case 8: return launch_t<D, 8>(a, w, st);
+    case 1: return launch_g<D, 1>(a, w, st);
+    case 2: return launch_g<D, 2>(a, w, st);
+    case 4: return launch_g<D, 4>(a, w, st);
+    case 8: return launch_g<D, 8>(a, w, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -60,7 +60,7 @@ extern "C" int pa_set_option(int32_t id, int64_t value) {
       pa::g_target_items = value;
       return PA_OK;
     case PA_OPT_DECODE_BUFFERS:
-      if (value < 0 || value > 2) return pa::fail(PA_ERR_INVALID, "PA_OPT_DECODE_BUFFERS takes 0, 1 or 2");
+      if (value < 0 || value > 4) return pa::fail(PA_ERR_INVALID, "PA_OPT_DECODE_BUFFERS takes 0..4");
       pa::g_decode_buffers = value;
       return PA_OK;
     case PA_OPT_DECODE_KERNEL:

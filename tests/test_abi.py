@@ -112,7 +112,7 @@ def test_options_roundtrip_and_errors():
     with pytest.raises(pk.PAError):
         pk.pa_set_option(pk.PA_OPT_FORCE_ROWWISE, 2)
     with pytest.raises(pk.PAError):
-        pk.pa_set_option(pk.PA_OPT_DECODE_BUFFERS, 3)
+        pk.pa_set_option(pk.PA_OPT_DECODE_BUFFERS, 5)
     with pytest.raises(pk.PAError):
         pk.pa_set_option(pk.PA_OPT_DECODE_KERNEL, -1)
     with pytest.raises(pk.PAError):

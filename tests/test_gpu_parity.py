@@ -104,10 +104,11 @@ def test_attention_random_steps(seed):
         _check_attention(spec, ds, out)
 
 
-@pytest.mark.parametrize("kernel,nbuf", [(1, 1), (1, 2), (2, 0)])
+@pytest.mark.parametrize("kernel,nbuf", [(1, 1), (1, 2), (2, 2), (2, 3), (2, 4)])
 @pytest.mark.parametrize("seed", [100, 101, 102, 103])
 def test_bf16_decode_kernels_match_oracle(seed, kernel, nbuf):
-    """Both row-wise kernels for bf16 (VALU with one or two page buffers, MFMA),
+    """Both row-wise kernels for bf16 (VALU with one or two page buffers, MFMA with
+    two to four),
     every group size, ranges both shorter and longer than a row."""
     r = np.random.default_rng(seed)
     hkv = [1, 2, 4, 2][seed % 4]
