@@ -246,9 +246,16 @@ extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_ca
   a.nb = num_blocks;
   a.bf16 = bf16 ? 1 : 0;
   a.merge_rows = pa_args.verify_rows;
+  // a small decode-only step on the MFMA decode kernel skips the plan kernel:
+  // every decode workgroup plans the (few) rows itself
+  a.self_plan = max_query_len <= 1 && bf16 && decode_uses_mfma(1) && num_tokens <= kSelfPlanRows &&
+                num_seqs <= kSelfPlanRows;
+  a.fixed_units = pa_args.fixed_units;
+  a.num_ranges = pa_args.num_ranges;
+  a.max_len = pa_args.max_len;
 
-  hipError_t e;
-  {
+  hipError_t e = hipSuccess;
+  if (!a.self_plan) {
     KernelTimer t(PA_K_PLAN, st);
     e = launch_plan(pa_args, w, st);
   }

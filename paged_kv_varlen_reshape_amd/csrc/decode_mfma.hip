@@ -94,7 +94,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D, int G, int NBUF>
+template <int D, int G, int NBUF, bool SELF>
 __global__ void __launch_bounds__(kThreads, 2)
 decode_mfma_kernel(AttnArgs a, Workspace w) {
   using C = DecM<D>;
@@ -137,18 +137,130 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
   // DMA: in instruction j of a page, lane -> row j*RPI + lane/CH, LDS chunk lane%CH
   const int dma_row = lane / CH, dma_chunk = lane % CH;
 
-  const int nranges = w.hdr[H_RANGES];
-  const int64_t units = w.hdr64[H64_UNITS];
-  const int64_t per = w.hdr64[H64_PER];
+  int nranges = SELF ? 0 : w.hdr[H_RANGES];
+  int64_t units = SELF ? 0 : w.hdr64[H64_UNITS];
+  int64_t per = SELF ? 1 : w.hdr64[H64_PER];
   const char* kbase = static_cast<const char*>(a.kc);
   const char* vbase = static_cast<const char*>(a.vc);
+
+  // A small decode-only step is planned here, by every workgroup for itself,
+  // instead of by the plan kernel: the row records and their first units go
+  // to LDS (workgroup 0 also stores them, and the step's header, for the
+  // merge), and each range finds its first row by binary search.  Same
+  // records, units and ranges as the plan kernel's.
+  __shared__ int4 s_rec[SELF ? kSelfPlanRows : 1];
+  __shared__ int64_t s_base[SELF ? kSelfPlanRows : 1];
+  __shared__ int64_t s_tot[2 * kWaves];
+  int nrec = 0;
+  if constexpr (SELF) {
+    const int tid = threadIdx.x;
+    const int64_t hkv = a.hkv;
+    constexpr int SPT = kSelfPlanRows / kThreads;  // sequences per thread
+    int32_t r0s[SPT], qs[SPT], cs[SPT];
+    int64_t nr = 0, nu = 0;
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int i = tid * SPT + k;
+      int32_t r0 = 0, q = 0, c = 0;
+      if (i < a.num_seqs) {  // clamped as the plan clamps them
+        r0 = a.qsl[i];
+        q = int32_t(min(int64_t(max(a.qsl[i + 1] - r0, 0)), int64_t(a.num_tokens) - r0));
+        if (r0 < 0 || r0 >= a.num_tokens) q = 0;
+        c = max(a.ctx[i], 0);
+        if (int64_t(c) + q > a.max_len) q = c >= a.max_len ? 0 : a.max_len - c;
+      }
+      r0s[k] = r0;
+      qs[k] = q;
+      cs[k] = c;
+      nr += q;
+      nu += hkv * (pages_upto(int64_t(c) + q) - pages_upto(c));
+    }
+    // exclusive scans of (rows, units) over the workgroup
+    int64_t ir = nr, iu = nu;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int64_t xr = __shfl_up(ir, d), xu = __shfl_up(iu, d);
+      if (lane >= d) {
+        ir += xr;
+        iu += xu;
+      }
+    }
+    if (lane == kWave - 1) {
+      s_tot[wave] = ir;
+      s_tot[kWaves + wave] = iu;
+    }
+    __syncthreads();
+    int64_t br = 0, bu = 0, tr = 0, tu = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      br += ww < wave ? s_tot[ww] : 0;
+      bu += ww < wave ? s_tot[kWaves + ww] : 0;
+      tr += s_tot[ww];
+      tu += s_tot[kWaves + ww];
+    }
+    int64_t r = br + ir - nr, u = bu + iu - nu;
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      for (int32_t j = 0; j < qs[k] && r < kSelfPlanRows; ++j, ++r) {
+        const int32_t len = cs[k] + j + 1;
+        s_rec[r] = make_int4(r0s[k] + j, tid * SPT + k, len, 1);
+        s_base[r] = u;
+        u += hkv * ((len + kBlock - 1) / kBlock);
+      }
+    }
+    __syncthreads();
+    nrec = int(min(tr, int64_t(kSelfPlanRows)));
+    units = tu;
+    per = a.fixed_units > 0 ? a.fixed_units : (units + a.num_ranges - 1) / a.num_ranges;
+    if (per < 1) per = 1;
+    int64_t n_r = (units + per - 1) / per;
+    if (n_r > w.ranges_cap) {
+      per = (units + w.ranges_cap - 1) / w.ranges_cap;
+      n_r = (units + per - 1) / per;
+    }
+    nranges = int(n_r);
+    if (blockIdx.x == 0) {
+      for (int rr = tid; rr < nrec; rr += kThreads) {
+        w.rows[rr] = s_rec[rr];
+        w.rows_base[rr] = s_base[rr];
+      }
+      if (tid == 0) {
+        w.hdr[H_ROWS] = nrec;
+        w.hdr[H_TILES] = 0;
+        w.hdr[H_RANGES] = nranges;
+        w.hdr64[H64_UNITS] = units;
+        w.hdr64[H64_PER] = per;
+      }
+    }
+  }
+  auto rec_at = [&](int r) __attribute__((always_inline)) -> int4 { return SELF ? s_rec[r] : w.rows[r]; };
+  auto base_at = [&](int r) __attribute__((always_inline)) -> int64_t { return SELF ? s_base[r] : w.rows_base[r]; };
 
   for (int g = gwave; g < nranges; g += nwaves) {
     int64_t x = g * per;
     const int64_t x_end = min(x + per, units);
-    int r = w.range_row[g];
-    int4 rec = w.rows[r];
-    int64_t base = w.rows_base[r];
+    int r;
+    if constexpr (SELF) {
+      // the last row whose first unit is at or before x
+      int lo = 0, hi = nrec;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_base[mid] <= x) lo = mid;
+        else hi = mid;
+      }
+      r = lo;
+      // the range's cut record for the merge: a start `off` units into its
+      // (row, kv head) is the first boundary strictly inside it iff 0 < off <= per
+      const int pg = (s_rec[r].z + kBlock - 1) / kBlock;
+      const int64_t rel = x - s_base[r];
+      const int k = int(rel / pg);
+      const int64_t off = rel - int64_t(k) * pg;
+      if (lane == 0) w.range_cut[g] = off > 0 && off <= per ? make_int2(r, k) : make_int2(-1, -1);
+    } else {
+      r = w.range_row[g];
+    }
+    int4 rec = rec_at(r);
+    int64_t base = base_at(r);
     int pages = (rec.z + kBlock - 1) / kBlock;
     int kvh = int((x - base) / pages);
     int p0 = int(x - base - int64_t(kvh) * pages);
@@ -301,8 +413,8 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
         p0 = 0;
         if (++kvh == a.hkv) {
           kvh = 0;
-          rec = w.rows[++r];
-          base = w.rows_base[r];
+          rec = rec_at(++r);
+          base = base_at(r);
           pages = (rec.z + kBlock - 1) / kBlock;
         }
       }
@@ -315,7 +427,8 @@ int resident_waves_t() {
   static int per_cu = 0;  // resident workgroups per CU, from the occupancy calculator
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<D, G, NBUF>, kThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<D, G, NBUF, false>, kThreads, 0) !=
+            hipSuccess ||
         n <= 0)
       n = 1;
     per_cu = n;
@@ -329,8 +442,15 @@ template <int D, int G, int NBUF>
 hipError_t launch_t(const AttnArgs& a, const Workspace& w, hipStream_t st) {
   int64_t waves = resident_waves_t<D, G, NBUF>();
   if (waves > w.ranges_cap) waves = w.ranges_cap;
+  if (a.self_plan) {  // its ranges are at most the requested count: launch just those wavefronts
+    const int64_t want = a.fixed_units > 0 ? w.ranges_cap : a.num_ranges;
+    if (waves > want) waves = want;
+  }
   const int64_t grid = (waves + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL((decode_mfma_kernel<D, G, NBUF>), dim3(unsigned(grid)), dim3(kThreads), 0, st, a, w);
+  if (a.self_plan)
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G, 2, true>), dim3(unsigned(grid)), dim3(kThreads), 0, st, a, w);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G, NBUF, false>), dim3(unsigned(grid)), dim3(kThreads), 0, st, a, w);
   return hipGetLastError();
 }
 

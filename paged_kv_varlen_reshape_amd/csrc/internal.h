@@ -93,6 +93,17 @@ struct PlanArgs {
 };
 hipError_t launch_plan(const PlanArgs& a, const Workspace& w, hipStream_t st);
 
+// Units (pages of 16 keys) of the rows whose key counts are 1..n:
+// sum over p = 1..n of ceil(p / 16).
+__device__ __forceinline__ int64_t pages_upto(int64_t n) {
+  const int64_t a = n / kBlock, b = n - a * kBlock;
+  return kBlock * a * (a + 1) / 2 + b * (a + 1);
+}
+
+// Most rows (and sequences) of a decode-only step that the MFMA decode kernel
+// plans by itself, without the plan kernel.
+constexpr int kSelfPlanRows = 512;
+
 struct AttnArgs {
   const void* q;
   const void* kc;
@@ -107,6 +118,8 @@ struct AttnArgs {
   int64_t nb;
   int32_t bf16;
   int32_t merge_rows;  // most query rows of one row-wise record this step (the plan's verify_rows)
+  int32_t self_plan;   // 1: decode-only step the MFMA decode kernel plans by itself (no plan kernel)
+  int32_t fixed_units, num_ranges, max_len;  // the plan's range parameters, for self_plan
 };
 hipError_t launch_decode(const AttnArgs& a, const Workspace& w, int group, hipStream_t st);
 // Resident decode wavefronts on the current device for this kernel instance.

@@ -63,12 +63,6 @@ __device__ void block_exclusive_scan2(int64_t x, int64_t y, int64_t* ox, int64_t
   __syncthreads();
 }
 
-// Units (pages of 16 keys) of the rows whose key counts are 1..n:
-// sum over p = 1..n of ceil(p / 16).
-__device__ __forceinline__ int64_t pages_upto(int64_t n) {
-  const int64_t a = n / kBlock, b = n - a * kBlock;
-  return kBlock * a * (a + 1) / 2 + b * (a + 1);
-}
 
 struct SeqInfo {
   int32_t r0, q, c;
