@@ -202,6 +202,24 @@ int pa_allocate_slots(pa_pool* pool, int64_t req, int64_t num_computed, int64_t 
 int pa_share_prefix(pa_pool* pool, int64_t req, const int32_t* ids, int32_t n);
 /* Release every block reference of `req` and forget it (unknown req: no-op). */
 int pa_free(pa_pool* pool, int64_t req);
+/* Prefix cache (Inside vLLM summary, section "高度な機能群", Prefix Caching: a
+ * request that starts with the same prompt reuses the cached KV blocks; the
+ * block pool holds the index).  A full block may be registered under a 64-bit
+ * key the caller computes (e.g. a hash of its tokens chained with the previous
+ * block's key).  A block released to zero references keeps its key and stays
+ * findable until the free queue hands it out again, which drops the key.
+ *
+ * pa_prefix_match: for a request holding no blocks, append the blocks cached
+ * under keys[0], keys[1], ... up to the first miss, one reference each (a
+ * released block is taken out of the free queue); *n_hit (host) receives the
+ * number of blocks reused.  keys: host, n entries.
+ * pa_prefix_register: register the request's first n blocks under keys[0..n)
+ * (host); a key already cached for another block keeps that block; a block
+ * already cached under a different key is an error (PA_ERR_INVALID, nothing
+ * changed).  pa_prefix_cached: blocks in the index (-1 for a null pool). */
+int pa_prefix_match(pa_pool* pool, int64_t req, const uint64_t* keys, int32_t n, int32_t* n_hit);
+int pa_prefix_register(pa_pool* pool, int64_t req, const uint64_t* keys, int32_t n);
+int64_t pa_prefix_cached(const pa_pool* pool);
 int64_t pa_num_free(const pa_pool* pool);
 /* Number of blocks request `req` holds (0 if unknown). */
 int32_t pa_num_req_blocks(const pa_pool* pool, int64_t req);

@@ -16,6 +16,12 @@ the request's blocks, in the request's block order, and appends every block
 whose count reaches zero to the tail of the queue.  Prefix caching (Inside vLLM
 summary, "高度な機能群") lets requests reuse cached KV blocks: ``share_prefix``
 appends already-allocated blocks to a request and adds one reference to each.
+The prefix cache index (that section, and the architecture overview's block
+pool holding it): ``prefix_register`` files a request's full blocks under
+caller keys; ``prefix_match`` gives a new request the blocks of its leading
+keys, one reference each, up to the first miss.  A block released to zero
+references keeps its key and stays findable until the queue hands it out
+again (which drops the key); a hit on such a block takes it out of the queue.
 
 Slot of the token at absolute position ``pos`` of a request:
 ``block_list[pos // block_size] * block_size + pos % block_size``.
@@ -40,6 +46,8 @@ class RefBlockPool:
         self.free_block_queue: deque = deque(order)
         self.req_to_blocks: Dict[int, List[int]] = {}
         self.refcount = [0] * num_blocks
+        self.cache: Dict[int, int] = {}  # key -> block
+        self.block_key: Dict[int, int] = {}  # block -> key
 
     # -- allocation ---------------------------------------------------------
     def blocks_needed(self, req: int, num_computed: int, num_new: int) -> int:
@@ -55,6 +63,8 @@ class RefBlockPool:
             return None  # caller must preempt; nothing changed
         new = [self.free_block_queue.popleft() for _ in range(n)]
         for b in new:
+            if b in self.block_key:  # reused: its cached contents go away
+                del self.cache[self.block_key.pop(b)]
             self.refcount[b] = 1
         self.req_to_blocks.setdefault(req, []).extend(new)
         return new
@@ -73,6 +83,40 @@ class RefBlockPool:
             self.refcount[b] -= 1
             if self.refcount[b] == 0:
                 self.free_block_queue.append(b)
+
+    # -- prefix cache -------------------------------------------------------
+    def prefix_match(self, req: int, keys) -> int:
+        if self.req_to_blocks.get(req):
+            raise ValueError("request already holds blocks")
+        hits = 0
+        for k in keys:
+            b = self.cache.get(int(k))
+            if b is None:
+                break
+            if self.refcount[b] == 0:
+                self.free_block_queue.remove(b)
+            self.refcount[b] += 1
+            self.req_to_blocks.setdefault(req, []).append(b)
+            hits += 1
+        return hits
+
+    def prefix_register(self, req: int, keys) -> None:
+        ids = self.req_to_blocks.get(req, [])
+        keys = [int(k) for k in keys]
+        if len(keys) > len(ids):
+            raise ValueError("request holds fewer blocks than keys")
+        for k, b in zip(keys, ids):
+            if b in self.block_key and self.block_key[b] != k:
+                raise ValueError(f"block {b} is cached under another key")
+        for k, b in zip(keys, ids):
+            if b in self.block_key or k in self.cache:
+                continue
+            self.cache[k] = b
+            self.block_key[b] = k
+
+    @property
+    def num_cached(self) -> int:
+        return len(self.cache)
 
     # -- queries ------------------------------------------------------------
     @property

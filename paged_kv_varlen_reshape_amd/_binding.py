@@ -35,6 +35,7 @@ KERNEL_NAMES = ["reshape_and_cache", "plan", "chunk_mfma", "decode", "split_merg
 
 _i32, _i64, _f32, _vp, _sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
 _pi32 = C.POINTER(C.c_int32)
+_pu64 = C.POINTER(C.c_uint64)
 
 # name -> (restype, argtypes); mirrors include/pa.h
 SIGNATURES = {
@@ -56,6 +57,9 @@ SIGNATURES = {
     "pa_share_prefix": (_i32, [_vp, _i64, _pi32, _i32]),
     "pa_free": (_i32, [_vp, _i64]),
     "pa_num_free": (_i64, [_vp]),
+    "pa_prefix_match": (_i32, [_vp, _i64, _pu64, _i32, _pi32]),
+    "pa_prefix_register": (_i32, [_vp, _i64, _pu64, _i32]),
+    "pa_prefix_cached": (_i64, [_vp]),
     "pa_num_req_blocks": (_i32, [_vp, _i64]),
     "pa_refcount": (_i32, [_vp, _i32]),
     "pa_block_table_row": (_i32, [_vp, _i64, _pi32, _i32, _i32]),
@@ -270,6 +274,22 @@ class BlockPool:
 
     def free(self, req: int) -> None:
         _check(lib().pa_free(self._h, req))
+
+    def prefix_match(self, req: int, keys) -> int:
+        """Reuse the cached blocks of the leading keys (up to the first miss); returns how many."""
+        k = np.ascontiguousarray(keys, dtype=np.uint64)
+        n = C.c_int32(0)
+        _check(lib().pa_prefix_match(self._h, req, k.ctypes.data_as(_pu64), k.size, C.byref(n)))
+        return int(n.value)
+
+    def prefix_register(self, req: int, keys) -> None:
+        """Register the request's first len(keys) blocks under these keys."""
+        k = np.ascontiguousarray(keys, dtype=np.uint64)
+        _check(lib().pa_prefix_register(self._h, req, k.ctypes.data_as(_pu64), k.size))
+
+    @property
+    def num_cached(self) -> int:
+        return int(lib().pa_prefix_cached(self._h))
 
     @property
     def num_free(self) -> int:

@@ -13,9 +13,20 @@
 // to the tail of the queue.  Prefix caching (Inside vLLM summary, "高度な機能群")
 // shares already cached blocks between requests with one reference each.
 //
-// The free queue is a ring buffer of block ids (capacity num_blocks, since a
-// block is in the queue at most once), so allocation and release are O(blocks
-// moved) with no per-call heap traffic beyond the request's own vector.
+// Prefix cache index (Inside vLLM summary, "高度な機能群", Prefix Caching: a
+// request that starts with the same prompt reuses the cached KV blocks; the
+// architecture overview places that index in the block pool).  A full block
+// can be registered under a caller-computed 64-bit key (for instance a hash
+// of its tokens chained with the key of the block before it); a new request
+// takes over the longest run of leading blocks whose keys hit, one reference
+// each.  A block whose references drop to zero keeps its contents and its key:
+// it waits in the free queue like any free block and stays findable until the
+// queue hands it out again, which removes its key (a hit on such a block
+// takes it out of the queue).
+//
+// The free queue is an intrusive doubly-linked list over block ids (sentinel
+// num_blocks), so allocation, release and taking a cached block out of the
+// queue are O(1) per block.
 #include <cstring>
 #include <unordered_map>
 #include <vector>
@@ -25,23 +36,36 @@
 struct pa_pool {
   int64_t num_blocks;
   int32_t block_size;
-  std::vector<int32_t> ring;  // free queue storage
-  int64_t head = 0;           // index of the first free block in `ring`
-  int64_t count = 0;          // blocks in the queue
+  std::vector<int32_t> next, prev;  // free queue links, [num_blocks + 1]
+  int64_t count = 0;                // blocks in the queue
   std::vector<int32_t> refcount;
   std::unordered_map<int64_t, std::vector<int32_t>> req_to_blocks;
+  std::unordered_map<uint64_t, int32_t> cache;  // key -> block
+  std::vector<uint64_t> block_key;
+  std::vector<char> has_key;
 
-  int32_t pop_front() {
-    int32_t b = ring[head];
-    head = (head + 1 == num_blocks) ? 0 : head + 1;
-    --count;
-    return b;
-  }
+  int32_t sentinel() const { return int32_t(num_blocks); }
   void push_back(int32_t b) {
-    int64_t tail = head + count;
-    if (tail >= num_blocks) tail -= num_blocks;
-    ring[tail] = b;
+    const int32_t s = sentinel(), t = prev[s];
+    next[t] = b;
+    prev[b] = t;
+    next[b] = s;
+    prev[s] = b;
     ++count;
+  }
+  void unlink(int32_t b) {
+    next[prev[b]] = next[b];
+    prev[next[b]] = prev[b];
+    --count;
+  }
+  int32_t pop_front() {  // the block leaves the cache index, its contents will be overwritten
+    const int32_t b = next[sentinel()];
+    unlink(b);
+    if (has_key[b]) {
+      cache.erase(block_key[b]);
+      has_key[b] = 0;
+    }
+    return b;
   }
 };
 
@@ -58,8 +82,12 @@ extern "C" pa_pool* pa_pool_create(int64_t num_blocks, int32_t block_size, const
   pa_pool* p = new pa_pool;
   p->num_blocks = num_blocks;
   p->block_size = block_size;
-  p->ring.resize(num_blocks);
+  p->next.assign(num_blocks + 1, 0);
+  p->prev.assign(num_blocks + 1, 0);
+  p->next[num_blocks] = p->prev[num_blocks] = int32_t(num_blocks);  // empty queue
   p->refcount.assign(num_blocks, 0);
+  p->block_key.assign(num_blocks, 0);
+  p->has_key.assign(num_blocks, 0);
   if (initial_order) {
     std::vector<char> seen(num_blocks, 0);
     for (int64_t i = 0; i < num_blocks; ++i) {
@@ -71,12 +99,11 @@ extern "C" pa_pool* pa_pool_create(int64_t num_blocks, int32_t block_size, const
         return nullptr;
       }
       seen[b] = 1;
-      p->ring[i] = b;
     }
+    for (int64_t i = 0; i < num_blocks; ++i) p->push_back(initial_order[i]);
   } else {
-    for (int64_t i = 0; i < num_blocks; ++i) p->ring[i] = int32_t(i);
+    for (int64_t i = 0; i < num_blocks; ++i) p->push_back(int32_t(i));
   }
-  p->count = num_blocks;
   return p;
 }
 
@@ -136,6 +163,53 @@ extern "C" int pa_free(pa_pool* pool, int64_t req) {
   pool->req_to_blocks.erase(it);
   return PA_OK;
 }
+
+extern "C" int pa_prefix_match(pa_pool* pool, int64_t req, const uint64_t* keys, int32_t n, int32_t* n_hit) {
+  pa::clear_error();
+  if (n_hit) *n_hit = 0;
+  if (!pool) return pa::fail(PA_ERR_INVALID, "pa_prefix_match: null pool");
+  if (n < 0 || (n > 0 && !keys)) return pa::fail(PA_ERR_INVALID, "pa_prefix_match: bad key list");
+  auto it = pool->req_to_blocks.find(req);
+  if (it != pool->req_to_blocks.end() && !it->second.empty())
+    return pa::fail(PA_ERR_INVALID, "pa_prefix_match: request %lld already holds blocks", (long long)req);
+  int32_t hits = 0;
+  for (; hits < n; ++hits) {
+    auto c = pool->cache.find(keys[hits]);
+    if (c == pool->cache.end()) break;
+    const int32_t b = c->second;
+    if (pool->refcount[b] == 0) pool->unlink(b);  // a released block waiting in the queue
+    pool->refcount[b] += 1;
+    pool->req_to_blocks[req].push_back(b);
+  }
+  if (n_hit) *n_hit = hits;
+  return PA_OK;
+}
+
+extern "C" int pa_prefix_register(pa_pool* pool, int64_t req, const uint64_t* keys, int32_t n) {
+  pa::clear_error();
+  if (!pool) return pa::fail(PA_ERR_INVALID, "pa_prefix_register: null pool");
+  if (n < 0 || (n > 0 && !keys)) return pa::fail(PA_ERR_INVALID, "pa_prefix_register: bad key list");
+  auto it = pool->req_to_blocks.find(req);
+  const int64_t have = it == pool->req_to_blocks.end() ? 0 : int64_t(it->second.size());
+  if (n > have)
+    return pa::fail(PA_ERR_INVALID, "pa_prefix_register: request %lld holds %lld blocks < %d", (long long)req,
+                    (long long)have, n);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = it->second[i];
+    if (pool->has_key[b] && pool->block_key[b] != keys[i])
+      return pa::fail(PA_ERR_INVALID, "pa_prefix_register: block %d is cached under another key", b);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = it->second[i];
+    if (pool->has_key[b] || pool->cache.count(keys[i])) continue;  // already there, or an equal block is
+    pool->cache.emplace(keys[i], b);
+    pool->block_key[b] = keys[i];
+    pool->has_key[b] = 1;
+  }
+  return PA_OK;
+}
+
+extern "C" int64_t pa_prefix_cached(const pa_pool* pool) { return pool ? int64_t(pool->cache.size()) : -1; }
 
 extern "C" int64_t pa_num_free(const pa_pool* pool) { return pool ? pool->count : -1; }
 

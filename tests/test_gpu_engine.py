@@ -1,6 +1,8 @@
 """Multi-step engine loop on the GPU: continuous batching with chunked prefill,
-preemption by recompute and block reuse, all steps writing into one persistent
-device pool through pa_reshape_and_cache and reading it through pa_attention.
+preemption by recompute and block reuse (and, in two cases, the pool's prefix
+index: requests reuse the cached blocks of a shared system prompt and their own
+released blocks), all steps writing into one persistent device pool through
+pa_reshape_and_cache and reading it through pa_attention.
 
 Every step's output is compared with the fp64 oracle computed from each
 request's regenerated K/V (max-abs 1e-5 for fp32, 1e-2 for bf16), and after
@@ -25,9 +27,13 @@ def _i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
-@pytest.mark.parametrize("dtype,hq,hkv,d,seed", [("f32", 8, 2, 64, 0), ("bf16", 8, 2, 128, 1)])
-def test_engine_loop_matches_oracle_every_step(dtype, hq, hkv, d, seed):
-    cfg = W.EngineConfig(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype=dtype, seed=seed)
+@pytest.mark.parametrize("dtype,hq,hkv,d,seed,cache", [("f32", 8, 2, 64, 0, False), ("bf16", 8, 2, 128, 1, False),
+                                                      ("f32", 8, 2, 64, 2, True), ("bf16", 8, 2, 128, 3, True)])
+def test_engine_loop_matches_oracle_every_step(dtype, hq, hkv, d, seed, cache):
+    """With ``cache`` the pool's prefix index is on and 70 % of the requests start with a
+    48-token system prompt: reused blocks must hold the K/V their keys name."""
+    cfg = W.EngineConfig(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype=dtype, seed=seed,
+                         prefix_cache=cache, shared_prefix=48 if cache else 0, share_fraction=0.7 if cache else 0.0)
     eng = W.EngineLoop(cfg, pk.BlockPool(cfg.num_blocks, 16, None))
     shape = (cfg.num_blocks, hkv, 16, d)
     kc = poison_fill(shape, dtype, "cuda")
@@ -64,7 +70,9 @@ def test_engine_loop_matches_oracle_every_step(dtype, hq, hkv, d, seed):
             worst = max(worst, err)
             assert err <= TOL[dtype], f"step {st.index} request {r.key}: {err:.3e}"
     torch.cuda.synchronize()
-    print(f"engine {dtype}: {nsteps} steps, {eng.preemptions} preemptions, max_abs_err={worst:.3e}", flush=True)
+    print(f"engine {dtype} cache={cache}: {nsteps} steps, {eng.preemptions} preemptions, "
+          f"{eng.cache_hits} reused blocks, max_abs_err={worst:.3e}", flush=True)
     assert eng.preemptions > 0
+    assert (eng.cache_hits > 0) == cache
     assert np.array_equal(kc.view(BITS_DT[dtype]).cpu().numpy().view(bdt), hk)
     assert np.array_equal(vc.view(BITS_DT[dtype]).cpu().numpy().view(bdt), hv)

@@ -16,6 +16,14 @@ C++ allocator through the binding, or the oracle's reference pool) in that
 order.  It holds none of the method's arithmetic.  Token values are a pure
 function of (request key, position) (values.py), so a recomputed request
 writes exactly the K/V it wrote before.
+
+With ``prefix_cache`` on, requests that share a system prompt (section
+"高度な機能群", Prefix Caching) find its full blocks in the pool's prefix index
+when they are admitted, and so do preempted requests find their own released
+blocks while the pool has not handed them out again; only the tokens past the
+reused blocks are computed.  Block keys stand in for the hash of a block's
+tokens chained with its predecessor's: the shared prompt's blocks have keys of
+their own, every other block a key of its request and position.
 """
 from __future__ import annotations
 
@@ -25,7 +33,7 @@ from typing import List, Optional
 
 import numpy as np
 
-from .configs import Request, StepSpec
+from .configs import PREFIX_KEY, Request, StepSpec
 from .step import StepMeta, step_rows
 
 
@@ -40,6 +48,7 @@ class EngineRequest:
     state: str = "waiting"  # waiting | running | finished
     admitted: int = -1  # admission order of the current run (-1 while waiting)
     preemptions: int = 0
+    shares_prefix: bool = False  # starts with the shared system prompt
 
     @property
     def total(self) -> int:
@@ -61,6 +70,9 @@ class EngineConfig:
     head_dim: int = 64
     dtype: str = "f32"
     seed: int = 0
+    prefix_cache: bool = False  # reuse cached full blocks at admission
+    shared_prefix: int = 0  # tokens of a system prompt some requests start with (multiple of 16)
+    share_fraction: float = 0.0
 
 
 @dataclass
@@ -87,12 +99,37 @@ class EngineLoop:
                           arrival=int(rng.integers(0, cfg.arrival_span)))
             for i in range(cfg.num_requests)
         ]
+        if cfg.shared_prefix:
+            share = np.random.default_rng((cfg.seed, 8)).random(cfg.num_requests) < cfg.share_fraction
+            for r, sh in zip(self.requests, share):
+                if sh:
+                    r.shares_prefix = True
+                    r.prompt += cfg.shared_prefix
         for r in self.requests:
             r.known = r.prompt
+        self.cache_hits = 0  # blocks reused from the prefix index
         self.step_index = 0
         self.admissions = 0
         self.table_rows = table_rows
         self.preemptions = 0
+
+    # -- prefix cache -------------------------------------------------------
+    def block_key(self, r: EngineRequest, i: int) -> int:
+        """Key of block i of request r (stands in for a chained hash of its tokens)."""
+        if r.shares_prefix and (i + 1) * 16 <= self.cfg.shared_prefix:
+            return (PREFIX_KEY << 32) | i
+        return (1 << 62) | (r.key << 32) | i
+
+    def _reuse_cached(self, r: EngineRequest) -> None:
+        """At admission: take over the cached blocks of the request's leading full blocks,
+        keeping the block of its last known token private (a step never writes into a
+        block another request may read)."""
+        n = (r.known - 1) // 16
+        if not self.cfg.prefix_cache or n <= 0 or r.computed:
+            return
+        hits = self.pool.prefix_match(r.key, [self.block_key(r, i) for i in range(n)])
+        r.computed = 16 * hits
+        self.cache_hits += hits
 
     # -- step formation ----------------------------------------------------
     def done(self) -> bool:
@@ -150,10 +187,13 @@ class EngineLoop:
                          and x.key not in preempted), key=lambda x: (x.arrival, x.key)):
             if budget == 0 or running >= cfg.max_running:
                 break
+            self._reuse_cached(r)
             q = min(want(r), budget)
             # a waiting request never preempts: it is admitted only if its blocks are free
             # (allocation is all or nothing, so a refusal leaves the pool unchanged)
             if self.pool.allocate_slots(r.key, r.computed, q) is None:
+                self.pool.free(r.key)  # the blocks it reused wait in the pool again
+                r.computed = 0
                 break
             r.state = "running"
             r.admitted = self.admissions
@@ -162,10 +202,10 @@ class EngineLoop:
             sched.append((r, q))
             budget -= q
 
-        reqs = [Request(r.key, r.computed, q) for r, q in sched]
+        reqs = [Request(r.key, r.computed, q, shares_prefix=r.shares_prefix) for r, q in sched]
         spec = StepSpec(f"engine step {self.step_index}", 2000 + cfg.seed, cfg.num_q_heads, cfg.num_kv_heads,
                         cfg.head_dim, cfg.dtype, 16, cfg.num_blocks, 1.0 / math.sqrt(cfg.head_dim), reqs,
-                        table_rows=self.table_rows, seed=2000 + cfg.seed)
+                        prefix_tokens=cfg.shared_prefix, table_rows=self.table_rows, seed=2000 + cfg.seed)
         qsl, seq_lens, ctx = step_rows(spec)
         width = max([spec.blocks_of(r) for r in reqs], default=1)
         bt = np.full((len(reqs), width), -1, dtype=np.int32)
@@ -179,6 +219,8 @@ class EngineLoop:
         # the step runs: its tokens are now cached; prompts done -> one token generated
         for r, q in sched:
             r.computed += q
+            if cfg.prefix_cache and r.computed // 16:  # its full blocks become findable
+                self.pool.prefix_register(r.key, [self.block_key(r, i) for i in range(r.computed // 16)])
             if r.computed >= r.prompt and r.known < r.total and r.computed == r.known:
                 r.known += 1
             if r.computed >= r.total:
