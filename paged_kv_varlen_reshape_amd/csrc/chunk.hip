@@ -72,7 +72,6 @@ typedef const __attribute__((address_space(4))) int32_t const_i32;  // read with
 constexpr int KLOOK = 2;  // K operand reads in flight ahead of the Q.K products
 
 // instruction classes of __builtin_amdgcn_sched_group_barrier
-constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
@@ -316,7 +315,10 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
       const char* vs = buf ? s_v1 : s_v0;
       const int key0 = kt * kBN;
 
-      // S^T = K Q^T: two 32-key blocks, the chains interleaved
+      // S^T = K Q^T: two 32-key blocks, the chains interleaved.  The products
+      // run at raised wave priority, so the matrix core is fed before the other
+      // wavefront's softmax when both are ready to issue
+      __builtin_amdgcn_s_setprio(1);
       f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
       {
         const char* kr = ks + col * RB;
@@ -337,6 +339,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * KLOOK, 0);
       }
+      __builtin_amdgcn_s_setprio(0);
       // causal mask (also hides keys past the tile's end): key > pos -> -inf;
       // accumulator row j of block mb is key key0 + lg*4 + mb*32 + (j/4)*8 + j%4
       if constexpr (decltype(masked)::value) {
@@ -384,6 +387,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
       // j = (t%2)*8 .. +8 of block t/2, i.e. keys 16t + (i/4)*8 + lg*4 + i%4,
       // loaded as two transposed quarters (i = 0..3: rows 16t + 4lg + k,
       // i = 4..7: rows 16t + 8 + 4lg + k)
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const u32x4 pb = {pk[t / 2][(t % 2) * 4 + 0], pk[t / 2][(t % 2) * 4 + 1], pk[t / 2][(t % 2) * 4 + 2],
@@ -401,6 +405,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
         }
       }
 
+      __builtin_amdgcn_s_setprio(0);
       // tile kt+1 has landed (and its tail is zeroed) before anyone reads it;
       // everyone is done with buffer buf before the DMA of tile kt+2 reuses it
       if (kt + 1 < n_kt) {
