@@ -30,7 +30,8 @@
  *   - dtype is PA_F32 or PA_BF16 and is the element type of q, k, v and both
  *     caches alike.  Outputs are always float32.
  *   - block_size must be 16; head_dim 64 or 128; num_q_heads a multiple of
- *     num_kv_heads with a group of 1, 2, 4 or 8; num_blocks * 16 < 2^31.
+ *     num_kv_heads with a group of 1, 2, 4 or 8; num_kv_heads < 2^15;
+ *     num_blocks * 16 < 2^31.
  *   - Cache layout: [num_blocks, num_kv_heads, 16, head_dim]; the token at
  *     slot s lives in block s / 16 at offset s % 16, so one (block, kv head)
  *     page of 16 tokens is one contiguous 16*head_dim run.

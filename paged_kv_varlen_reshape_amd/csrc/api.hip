@@ -70,7 +70,7 @@ namespace {
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 int check_dims(int32_t hkv, int32_t d, int32_t bs, int32_t dtype, int64_t nb, const char* who) {
-  if (hkv <= 0) return fail(PA_ERR_INVALID, "%s: num_kv_heads must be positive", who);
+  if (hkv <= 0 || hkv >= (1 << 15)) return fail(PA_ERR_INVALID, "%s: num_kv_heads %d out of range", who, hkv);
   if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d not supported", who, dtype);
   if (bs != kBlock) return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only 16 is built)", who, bs);
   if (d != 64 && d != 128) return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128 are built)", who, d);
@@ -126,7 +126,7 @@ Workspace layout_workspace(const StepShape& s, void* ws) {
   w.tiles = reinterpret_cast<int2*>(take(w.tiles_cap * sizeof(int2)));
   w.tiles_tmp = reinterpret_cast<int4*>(take(w.tiles_cap * sizeof(int4)));
   w.range_row = reinterpret_cast<int32_t*>(take(w.ranges_cap * sizeof(int32_t)));
-  w.range_cut = reinterpret_cast<int2*>(take(w.ranges_cap * sizeof(int2)));
+  w.range_cut = reinterpret_cast<int4*>(take(w.ranges_cap * sizeof(int4)));
   w.part_o = reinterpret_cast<float*>(take(size_t(2 * w.ranges_cap * w.ncol) * s.head_dim * sizeof(float)));
   w.part_ml = reinterpret_cast<float2*>(take(size_t(2 * w.ranges_cap * w.ncol) * sizeof(float2)));
   w.bytes = off;

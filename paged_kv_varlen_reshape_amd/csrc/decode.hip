@@ -320,78 +320,89 @@ decode_streamk_kernel(AttnArgs a, Workspace w) {
 }
 
 // split_merge: (record, kv head) pairs cut by range boundaries.  Range g's
-// start first cuts the pair (r, k) recorded for it; the pair's pieces are the
-// last segment of the range holding its first unit (slot 0 if that range
-// starts exactly there, else slot 1) and the first segment (slot 0) of every
-// later range up to the one holding its last unit.  One wavefront per (range,
-// query row of the record) folds the G heads of that row with a running
-// maximum:
+// start first cuts the pair whose merge record (cut_record) it holds; the
+// pair's parts are the last segment of the range g0 holding its first unit
+// (slot 0 if g0 starts exactly there, else slot 1) and the first segment
+// (slot 0) of every later range up to the one holding its last unit.  One
+// wavefront per (range, query row of the record) folds the G heads of that
+// row with a running maximum:
 //   M = max_s m_s;  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
-// Lane l owns E = G*D/64 consecutive elements of a row's G x D output (one
-// head each), so every piece is read with wide coalesced loads.  Slots hold
-// w.ncol columns (row j, head h is column j*G + h).
+// The record says everything the fold needs, so a wavefront makes two
+// dependent round trips: the record (with the range count beside it), then
+// the parts, kParts at a time.  Lane l owns E = G*D/64 consecutive elements of
+// a row's G x D output (one head each), so every part is read with wide
+// coalesced loads.  Slots hold w.ncol columns (row j, head h is column j*G + h).
+constexpr int kParts = 4;
+
 template <int D, int G>
 __global__ void __launch_bounds__(256)
-split_merge_kernel(AttnArgs a, Workspace w) {
+split_merge_kernel(AttnArgs a, Workspace w, int64_t max_ranges) {
   constexpr int E = G * D / kWave;  // elements per lane: 1..16
   constexpr int V4 = E >= 4 ? E / 4 : 0;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t nr = w.hdr[H_RANGES];
-  const int64_t per = w.hdr64[H64_PER];
   const int64_t ncol = w.ncol;
   const int vrows = a.merge_rows;  // most query rows of one record
   const int64_t waves = int64_t(gridDim.x) * (blockDim.x / kWave);
   const int e0 = lane * E;
   const int h = e0 / D;  // head of this lane's elements
-  for (int64_t gj = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave; gj < nr * vrows;
+  for (int64_t gj = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave; gj < max_ranges * vrows;
        gj += waves) {
     const int64_t g = gj / vrows;
     const int j = int(gj - g * vrows);
-    const int2 cut = w.range_cut[g];
-    if (g == 0 || cut.x < 0) continue;
-    const int4 rec = w.rows[cut.x];
-    if (j >= rec.w) continue;
-    const int64_t pages = (rec.z + kBlock - 1) / kBlock;
-    const int64_t f = w.rows_base[cut.x] + cut.y * pages;  // first unit of the pair
-    const int64_t g0 = f / per, g1 = (f + pages - 1) / per;
-    {
-      const int64_t c0 = int64_t(j) * G;  // the row's first column
-      float M = -INFINITY, lsum = 0.f, acc[E];
+    const int4 cut = w.range_cut[g];
+    const int nr = w.hdr[H_RANGES];
+    if (g >= nr || cut.x < 0 || j >= (cut.y >> 16)) continue;
+    const int kvh = cut.y & 0xFFFF;
+    const int64_t g0 = cut.z;
+    const int nparts = cut.w >> 1, s0 = cut.w & 1;
+    const int64_t c0 = int64_t(j) * G;  // the row's first column
+    float M = -INFINITY, lsum = 0.f, acc[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = 0.f;
-      for (int64_t gg = g0; gg <= g1; ++gg) {
-        const int64_t slot = gg * 2 + (gg == g0 && f != g0 * per ? 1 : 0);
-        const float2 ml = w.part_ml[slot * ncol + c0 + h];
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int p0 = 0; p0 < nparts; p0 += kParts) {
+      float2 ml[kParts];
+      float v[kParts][E];
+#pragma unroll
+      for (int p = 0; p < kParts; ++p) {
+        const bool have = p0 + p < nparts;
+        const int64_t slot = have ? (g0 + p0 + p) * 2 + (p0 + p == 0 ? s0 : 0) : 0;
         const float* po = w.part_o + (slot * ncol + c0) * D + e0;
-        float v[E];
-        if constexpr (V4 > 0) {
+        if (have) {
+          ml[p] = w.part_ml[slot * ncol + c0 + h];
+          if constexpr (V4 > 0) {
 #pragma unroll
-          for (int c = 0; c < V4; ++c) {
-            const float4 t = reinterpret_cast<const float4*>(po)[c];
-            v[4 * c] = t.x; v[4 * c + 1] = t.y; v[4 * c + 2] = t.z; v[4 * c + 3] = t.w;
+            for (int c = 0; c < V4; ++c) {
+              const float4 t = reinterpret_cast<const float4*>(po)[c];
+              v[p][4 * c] = t.x; v[p][4 * c + 1] = t.y; v[p][4 * c + 2] = t.z; v[p][4 * c + 3] = t.w;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[p][e] = po[e];
           }
-        } else {
-#pragma unroll
-          for (int e = 0; e < E; ++e) v[e] = po[e];
         }
-        const float Mn = fmaxf(M, ml.x);
-        const float fo = fast_exp2(M - Mn), fn = fast_exp2(ml.x - Mn);
-        lsum = lsum * fo + ml.y * fn;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = acc[e] * fo + v[e] * fn;
-        M = Mn;
       }
-      const float inv = 1.f / lsum;
-      float* op = a.out + (int64_t(rec.x + j) * a.hq + int64_t(cut.y) * G) * D + e0;
-      if constexpr (V4 > 0) {
 #pragma unroll
-        for (int c = 0; c < V4; ++c)
-          reinterpret_cast<float4*>(op)[c] =
-              make_float4(acc[4 * c] * inv, acc[4 * c + 1] * inv, acc[4 * c + 2] * inv, acc[4 * c + 3] * inv);
-      } else {
+      for (int p = 0; p < kParts; ++p) {
+        if (p0 + p < nparts) {
+          const float Mn = fmaxf(M, ml[p].x);
+          const float fo = fast_exp2(M - Mn), fn = fast_exp2(ml[p].x - Mn);
+          lsum = lsum * fo + ml[p].y * fn;
 #pragma unroll
-        for (int e = 0; e < E; ++e) op[e] = acc[e] * inv;
+          for (int e = 0; e < E; ++e) acc[e] = acc[e] * fo + v[p][e] * fn;
+          M = Mn;
+        }
       }
+    }
+    const float inv = 1.f / lsum;
+    float* op = a.out + (int64_t(cut.x + j) * a.hq + int64_t(kvh) * G) * D + e0;
+    if constexpr (V4 > 0) {
+#pragma unroll
+      for (int c = 0; c < V4; ++c)
+        reinterpret_cast<float4*>(op)[c] =
+            make_float4(acc[4 * c] * inv, acc[4 * c + 1] * inv, acc[4 * c + 2] * inv, acc[4 * c + 3] * inv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) op[e] = acc[e] * inv;
     }
   }
 }
@@ -423,12 +434,12 @@ hipError_t launch_decode_t(const AttnArgs& a, const Workspace& w, hipStream_t st
 
 template <int D, int G>
 hipError_t launch_merge_t(const AttnArgs& a, const Workspace& w, int64_t max_ranges, hipStream_t st) {
-  // one wavefront per (range, query row of a record): each merge is a short
-  // chain of dependent loads, so they all run side by side (a range without a
-  // cut exits at once)
+  // one wavefront per (range, query row of a record): each merge is two
+  // dependent round trips, so they all run side by side (a range without a
+  // cut exits after the first)
   if (max_ranges > w.ranges_cap) max_ranges = w.ranges_cap;
   const int64_t grid = (max_ranges * a.merge_rows + 3) / 4;
-  hipLaunchKernelGGL((split_merge_kernel<D, G>), dim3(unsigned(grid)), dim3(256), 0, st, a, w);
+  hipLaunchKernelGGL((split_merge_kernel<D, G>), dim3(unsigned(grid)), dim3(256), 0, st, a, w, max_ranges);
   return hipGetLastError();
 }
 

@@ -255,7 +255,9 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
       const int64_t rel = x - s_base[r];
       const int k = int(rel / pg);
       const int64_t off = rel - int64_t(k) * pg;
-      if (lane == 0) w.range_cut[g] = off > 0 && off <= per ? make_int2(r, k) : make_int2(-1, -1);
+      if (lane == 0)
+        w.range_cut[g] = off > 0 && off <= per ? cut_record(x - off, pg, per, s_rec[r].x, k, s_rec[r].w)
+                                               : make_int4(-1, -1, -1, -1);
     } else {
       r = w.range_row[g];
     }

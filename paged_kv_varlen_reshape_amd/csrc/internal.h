@@ -40,7 +40,7 @@ enum PlanHeader : int {
 // run of pages_r.  The stream is cut into ranges of equal length, one
 // wavefront each.  A (row, kv head) that a range boundary cuts leaves partial
 // results in two slots per range: slot 0 for the range's first segment, slot 1
-// for its last; split_merge folds them.
+// for its last; split_merge folds them, reading only the pair's merge record.
 struct Workspace {
   int64_t* hdr64;      // hdr + H64
   int32_t* hdr;        // [H_WORDS]
@@ -52,7 +52,8 @@ struct Workspace {
                        //   longest first
   int4* tiles_tmp;     // [tiles_cap]  plan scratch: tiles in sequence order with their bucket
   int32_t* range_row;  // [ranges_cap] row holding each range's first unit
-  int2* range_cut;     // [ranges_cap] {row, kv head} first cut by this range's start, or {-1, -1}
+  int4* range_cut;     // [ranges_cap] merge record of the (row, kv head) pair first cut by this
+                       //   range's start (cut_record), or x = -1
   float* part_o;       // [2 * ranges_cap * ncol * D] unnormalised partial outputs
   float2* part_ml;     // [2 * ranges_cap * ncol]     partial (max, sum), log2 domain
   int64_t rows_cap, tiles_cap, ranges_cap;
@@ -98,6 +99,17 @@ hipError_t launch_plan(const PlanArgs& a, const Workspace& w, hipStream_t st);
 __device__ __forceinline__ int64_t pages_upto(int64_t n) {
   const int64_t a = n / kBlock, b = n - a * kBlock;
   return kBlock * a * (a + 1) / 2 + b * (a + 1);
+}
+
+// Merge record of the (row, kv head) pair whose units are [f, f + pages) when
+// the range starting at g * per is the first boundary strictly inside it
+// (0 < g * per - f <= per): {first token row of the record, kv head | query
+// rows << 16, first range g0 of the pair, parts << 1 | slot of g0's part}.
+// The pair's parts are the segments of ranges g0 .. (f + pages - 1) / per;
+// g0's part is its last segment (slot 1) unless the pair starts g0 (slot 0).
+__device__ __forceinline__ int4 cut_record(int64_t f, int64_t pages, int64_t per, int tok, int kvh, int nq) {
+  const int64_t g0 = f / per, g1 = (f + pages - 1) / per;
+  return make_int4(tok, kvh | (nq << 16), int(g0), int(2 * (g1 - g0 + 1)) | (f != g0 * per ? 1 : 0));
 }
 
 // Most rows (and sequences) of a decode-only step that the MFMA decode kernel

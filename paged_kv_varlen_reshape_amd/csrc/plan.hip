@@ -106,6 +106,8 @@ plan_kernel(PlanArgs a, Workspace w) {
   __shared__ int s_hist[kSortBuckets];
   __shared__ int64_t s_base[kLdsRows];   // first unit of each row
   __shared__ int32_t s_pages[kLdsRows];  // pages of each row (per kv head)
+  __shared__ int32_t s_tok[kLdsRows];    // first token row of each record
+  __shared__ int8_t s_nq[kLdsRows];      // query rows of each record
   const int tid = threadIdx.x;
   const int64_t hkv = a.num_kv_heads;
 
@@ -147,6 +149,8 @@ plan_kernel(PlanArgs a, Workspace w) {
             if (r < kLdsRows) {
               s_base[r] = u;
               s_pages[r] = pages;
+              s_tok[r] = s.r0 + j;
+              s_nq[r] = int8_t(nq);
             }
             u += hkv * pages;
           }
@@ -189,8 +193,9 @@ plan_kernel(PlanArgs a, Workspace w) {
   }
 
   // pass 2: every range start names the row holding it and, if it is the
-  // first boundary strictly inside a (row, kv head) pair, the pair.  A start
-  // `off` units into its pair is that boundary iff 0 < off <= per.
+  // first boundary strictly inside a (row, kv head) pair, the pair's merge
+  // record.  A start `off` units into its pair is that boundary iff
+  // 0 < off <= per.
   if (rows <= kLdsRows) {
     // one thread per range: binary search of the rows' first units in LDS
     for (int64_t g = tid; g < nranges; g += kPlanThreads) {
@@ -204,13 +209,16 @@ plan_kernel(PlanArgs a, Workspace w) {
       const uint32_t rel = uint32_t(start - s_base[lo]), pages = uint32_t(s_pages[lo]);
       const uint32_t k = rel / pages, off = rel - k * pages;
       w.range_row[g] = lo;
-      w.range_cut[g] = off > 0 && off <= per ? make_int2(lo, int(k)) : make_int2(-1, -1);
+      w.range_cut[g] = off > 0 && off <= per
+                           ? cut_record(start - off, pages, per, s_tok[lo], int(k), s_nq[lo])
+                           : make_int4(-1, -1, -1, -1);
     }
   } else {
     // one thread per row: the range starts inside each of its pairs
     const double inv_per = 1.0 / double(per);
     for (int64_t r = tid; r < rows; r += kPlanThreads) {
-      const int64_t pages = (w.rows[r].z + kBlock - 1) / kBlock;
+      const int4 rec = w.rows[r];
+      const int64_t pages = (rec.z + kBlock - 1) / kBlock;
       for (int k = 0; k < hkv; ++k) {
         const int64_t start = w.rows_base[r] + k * pages;
         int64_t g = int64_t(double(start) * inv_per);  // first range starting at or after start
@@ -219,7 +227,8 @@ plan_kernel(PlanArgs a, Workspace w) {
         for (; g * per < start + pages && g < nranges; ++g) {
           const int64_t off = g * per - start;
           w.range_row[g] = int32_t(r);
-          w.range_cut[g] = off > 0 && off <= per ? make_int2(int32_t(r), k) : make_int2(-1, -1);
+          w.range_cut[g] = off > 0 && off <= per ? cut_record(start, pages, per, rec.x, k, rec.w)
+                                                 : make_int4(-1, -1, -1, -1);
         }
       }
     }
