@@ -87,12 +87,20 @@ __device__ __forceinline__ int v_swz(int row) {
   return (2 * (row & 3) + 8 * ((row >> 2) & 1)) & (CH - 1);
 }
 
+__device__ __forceinline__ void store_f4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store_f2(float2* p, float a, float b) { *p = make_float2(a, b); }
+
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their maxima)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+
+// pairs per self-planned range whose Q is loaded at the range's start
+constexpr int kQSlots = 4;
 
 template <int D, int G, int NBUF, bool SELF>
 __global__ void __launch_bounds__(kThreads, 2)
@@ -236,6 +244,237 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
   auto rec_at = [&](int r) __attribute__((always_inline)) -> int4 { return SELF ? s_rec[r] : w.rows[r]; };
   auto base_at = [&](int r) __attribute__((always_inline)) -> int64_t { return SELF ? s_base[r] : w.rows_base[r]; };
 
+  // O^T += V^T P^T for one page.  Keys at or past `nvalid` (the last, partly
+  // filled page of a row) may hold anything, so their V elements are zeroed
+  // in the operand registers: element j of a lane's transposed read is key
+  // 4grp + j of the page.
+  auto pv_page = [&](f32x4_t (&o)[DB], bf16x4_t pw, const char* vs, int nvalid) __attribute__((always_inline)) {
+    uint32_t m01 = ~0u, m23 = ~0u;
+    if (nvalid < kBlock) {
+      const int k0 = 4 * grp;
+      m01 = (k0 < nvalid ? 0xFFFFu : 0u) | (k0 + 1 < nvalid ? 0xFFFF0000u : 0u);
+      m23 = (k0 + 2 < nvalid ? 0xFFFFu : 0u) | (k0 + 3 < nvalid ? 0xFFFF0000u : 0u);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs + vaddr[db]));
+      uint2 u = __builtin_bit_cast(uint2, v);
+      u.x &= m01;
+      u.y &= m23;
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, u), pw, o[db], 0, 0, 0);
+    }
+  };
+
+  // A self-planned range streams its pages as one sequence across the (row,
+  // kv head) pairs it covers, with no memory round trip at a pair boundary:
+  // at the range's start one load per lane fetches the block id (and notes
+  // the kv head) of each of its first 64 pages, and the Q of its first
+  // kQSlots pairs comes into registers; the next pair's first page is then
+  // issued while the current pair's last page is multiplied.  Inside the
+  // loop only the page copies are loads in flight and LDS is touched only by
+  // the copies and the V operand reads, so the compiler's own waits stay
+  // per page.  (The records are in LDS; a decode record has one query row.)
+  auto flat_range = [&](int g, int64_t x, int64_t x_end, int r, int kvh, int p0) __attribute__((always_inline)) {
+    if constexpr (SELF) {
+      const int hkv = a.hkv;
+      const int total = int(x_end - x);
+      const bool col_ok = jrow < 1;
+      // (record fields are wave-uniform: read them into scalars)
+      auto pages_of = [&](int rr) __attribute__((always_inline)) {
+        return __builtin_amdgcn_readfirstlane((s_rec[rr].z + kBlock - 1) / kBlock);
+      };
+      auto next_pair = [&](int& rr, int& kh) __attribute__((always_inline)) {
+        if (++kh == hkv) {
+          kh = 0;
+          ++rr;
+        }
+      };
+      // Q of pair (rr, kh) as the B operand: lane holds head hq (zeros past the group), dims 8grp + 32kk
+      auto load_q = [&](int rr, int kh, u32x4 (&qq)[KS]) __attribute__((always_inline)) {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) +
+                                                         (int64_t(s_rec[rr].x) * a.hq + int64_t(kh) * G + hh) * RB);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) qq[kk] = col_ok ? qp[grp + 4 * kk] : u32x4{0u, 0u, 0u, 0u};
+      };
+
+      // page table of the stream, 64 pages at a time: lane j holds the block id
+      // and kv head of stream page f0 + j; (tr, tkh, tp) is the batch's first page
+      int tr = r, tkh = kvh, tp = p0;
+      int32_t ids = 0, khs = 0;
+      auto table = [&](int f0) __attribute__((always_inline)) {
+        int rr = tr, kh = tkh, p = tp + lane, pg = pages_of(rr);
+        const bool mine = f0 + lane < total;
+        while (mine && p >= pg) {
+          p -= pg;
+          next_pair(rr, kh);
+          pg = pages_of(rr);
+        }
+        ids = mine ? a.bt[int64_t(s_rec[rr].y) * a.mbps + p] : 0;
+        khs = kh;
+        if (f0 + kWave < total) {  // the next batch's first page
+          tp += kWave;
+          while (tp >= pages_of(tr)) {
+            tp -= pages_of(tr);
+            next_pair(tr, tkh);
+          }
+        }
+      };
+      table(0);
+      // Q of the range's first kQSlots pairs (a later pair's is loaded when it starts)
+      u32x4 qall[kQSlots][KS];
+      {
+        int rr = r, kh = kvh, left = total - (pages_of(r) - p0);
+#pragma unroll
+        for (int k = 0; k < kQSlots; ++k) {
+          if (k == 0 || left > 0) {
+            if (k > 0) {
+              next_pair(rr, kh);
+              left -= pages_of(rr);
+            }
+            load_q(rr, kh, qall[k]);
+          }
+        }
+      }
+      // the block ids are needed for the first page anyway; with the Q loads
+      // done too, the page loop starts with nothing else in flight
+      wait_vmcnt<0>();
+
+      auto issue = [&](int f, u32x4 (&kf)[KS], auto bufc) __attribute__((always_inline)) {
+        if (f > 0 && (f & (kWave - 1)) == 0) table(f);
+        const int32_t braw = __builtin_amdgcn_readlane(ids, f & (kWave - 1));
+        const int kh = __builtin_amdgcn_readlane(khs, f & (kWave - 1));
+        const int32_t b = braw < 0 ? 0 : (braw >= a.nb ? int32_t(a.nb - 1) : braw);  // never leave the pool
+        const int64_t pb = (int64_t(b) * hkv + kh) * PAGE;
+        char* dv = vbuf(bufc);
+#pragma unroll
+        for (int ii = 0; ii < IPG; ++ii) {
+          const int row = ii * RPI + dma_row;
+          const int64_t gv = pb + int64_t(row) * RB + 16 * (dma_chunk ^ v_swz<CH>(row));
+          __builtin_amdgcn_global_load_lds(vbase + gv, (lds_void_t*)(dv + ii * RPI * RB), 16, 0, 0);
+        }
+        const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + pb + int64_t(hq) * RB);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) kf[kk] = __builtin_nontemporal_load(kp + grp + 4 * kk);
+      };
+
+      // compute side: pair (cr, ckh) (the range's pair number cn), page cp; this range's part of it began at cp0
+      int cr = r, ckh = kvh, cn = 0, cp = p0, cp0 = p0, cleft = total, cpages = pages_of(r);
+      int clen = __builtin_amdgcn_readfirstlane(s_rec[r].z);
+      u32x4 qf[KS];
+      f32x4_t o[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = f32x4_t{};
+      float m = -INFINITY, l = 0.f;
+      auto compute = [&](const u32x4 (&kf)[KS], auto bufc) __attribute__((always_inline)) {
+        if (cp == cp0) {
+          if (cn < kQSlots) {
+#pragma unroll
+            for (int k = 0; k < kQSlots; ++k)
+              if (__builtin_amdgcn_readfirstlane(cn) == k) {
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) qf[kk] = qall[k][kk];
+              }
+          } else {
+            load_q(cr, ckh, qf);
+            wait_vmcnt<0>();  // rare (a range over many short pairs): keep the loop's waits per page
+          }
+        }
+        char* vs = vbuf(bufc);
+        const int pos0 = cp * kBlock;  // first key of the page
+        f32x4_t sc = f32x4_t{};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]),
+                                                      __builtin_bit_cast(bf16x8_t, qf[kk]), sc, 0, 0, 0);
+        const int kfirst = pos0 + 4 * grp;  // key of accumulator row 0 of this lane
+        const int lim = clen + jrow;        // keys this column's row sees
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = kfirst + i < lim ? sc[i] * a.scale_log2 : -INFINITY;
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (mx > m + 8.f) {  // lazy rescale: weights stay <= 2^8
+          const float alpha = fast_exp2(m - mx);
+          m = mx;
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        }
+        const float m_use = m == -INFINITY ? 0.f : m;
+        const uint32_t p01 = pack_bf16(fast_exp2(sc[0] - m_use), fast_exp2(sc[1] - m_use));
+        const uint32_t p23 = pack_bf16(fast_exp2(sc[2] - m_use), fast_exp2(sc[3] - m_use));
+        l += __uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u) + __uint_as_float(p23 << 16) +
+             __uint_as_float(p23 & 0xFFFF0000u);
+        const bf16x4_t pv = __builtin_bit_cast(bf16x4_t, make_uint2(p01, p23));
+        pv_page(o, pv, vs, clen - pos0);
+        --cleft;
+        if (++cp == cpages || cleft == 0) {
+          // this range's part of the pair is done: the four lane groups hold disjoint keys
+          float lt = l + __shfl_xor(l, 16);
+          lt += __shfl_xor(lt, 32);
+          const bool whole = cp0 == 0 && cp == cpages;
+          const int64_t slot = int64_t(g) * 2 + (cn == 0 ? 0 : 1);
+          if (col_ok) {
+            if (whole) {
+              const float inv = 1.f / lt;
+              float* op = a.out + (int64_t(s_rec[cr].x) * a.hq + int64_t(ckh) * G + hh) * D + 4 * grp;
+#pragma unroll
+              for (int db = 0; db < DB; ++db)
+                store_f4(op + 16 * db, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+            } else {
+              float* po = w.part_o + (slot * w.ncol + hq) * D + 4 * grp;
+#pragma unroll
+              for (int db = 0; db < DB; ++db)
+                store_f4(po + 16 * db, o[db][0], o[db][1], o[db][2], o[db][3]);
+              if (grp == 0) store_f2(w.part_ml + slot * w.ncol + hq, m, lt);
+            }
+          }
+          if (cleft > 0) {  // the next pair
+            next_pair(cr, ckh);
+            ++cn;
+            cp = 0;
+            cp0 = 0;
+            cpages = pages_of(cr);
+            clen = __builtin_amdgcn_readfirstlane(s_rec[cr].z);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db] = f32x4_t{};
+            m = -INFINITY;
+            l = 0.f;
+          }
+        }
+      };
+
+      // stream page f uses LDS buffer and K register set f % 2
+      u32x4 kset[2][KS];
+      issue(0, kset[0], Buf<0>{});
+      // page f + 1 flies while page f (landed) is multiplied
+      auto step = [&](int f, auto bufc) __attribute__((always_inline)) {
+        constexpr int B = decltype(bufc)::value;
+        issue(f + 1, kset[1 - B], Buf<1 - B>{});
+        wait_vmcnt<PER_PAGE>();
+        compute(kset[B], bufc);
+      };
+      // the last page: nothing flies behind it
+      auto last = [&](auto bufc) __attribute__((always_inline)) {
+        wait_vmcnt<0>();
+        compute(kset[decltype(bufc)::value], bufc);
+      };
+      // every pass of the loop runs two full steps (one path through it, so
+      // the compiler's own waits for the K registers stay per page)
+      int f = 0;
+      for (; f + 2 < total; f += 2) {
+        step(f, Buf<0>{});
+        step(f + 1, Buf<1>{});
+      }
+      if (f + 1 < total) {
+        step(f, Buf<0>{});
+        last(Buf<1>{});
+      } else {
+        last(Buf<0>{});
+      }
+    }
+  };
+
   for (int g = gwave; g < nranges; g += nwaves) {
     int64_t x = g * per;
     const int64_t x_end = min(x + per, units);
@@ -255,9 +494,13 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
       const int64_t rel = x - s_base[r];
       const int k = int(rel / pg);
       const int64_t off = rel - int64_t(k) * pg;
-      if (lane == 0)
-        w.range_cut[g] = off > 0 && off <= per ? cut_record(x - off, pg, per, s_rec[r].x, k, s_rec[r].w)
-                                               : make_int4(-1, -1, -1, -1);
+      if (lane == 0) {
+        const int4 c = off > 0 && off <= per ? cut_record(x - off, pg, per, s_rec[r].x, k, s_rec[r].w)
+                                             : make_int4(-1, -1, -1, -1);
+        w.range_cut[g] = c;
+      }
+      flat_range(g, x, x_end, r, k, int(off));
+      continue;
     } else {
       r = w.range_row[g];
     }
@@ -319,11 +562,6 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
       auto compute = [&](int j, const u32x4 (&kf)[KS], auto bufc) {
         char* vs = vbuf(bufc);
         const int pos0 = (p0 + j) * kBlock;  // first key of the page
-        if (pos0 + kBlock > len) {
-          // last, partly filled page: its V rows past the last row must not reach PV
-          for (int idx = lane; idx < kBlock * CH; idx += kWave)
-            if (pos0 + idx / CH >= len) *reinterpret_cast<u32x4*>(vs + idx * 16) = u32x4{0u, 0u, 0u, 0u};
-        }
         f32x4_t s = f32x4_t{};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
@@ -348,11 +586,7 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
         l += __uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u) + __uint_as_float(p23 << 16) +
              __uint_as_float(p23 & 0xFFFF0000u);
         const bf16x4_t pb = __builtin_bit_cast(bf16x4_t, make_uint2(p01, p23));
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs + vaddr[db]));
-          o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, v), pb, o[db], 0, 0, 0);
-        }
+        pv_page(o, pb, vs, len - pos0);
       };
 
       // pages j+1 .. j+NBUF-1 fly while page j is multiplied: page j uses
@@ -398,14 +632,13 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
           float* op = a.out + (int64_t(tok + jrow) * a.hq + int64_t(kvh) * G + hh) * D + 4 * grp;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            *reinterpret_cast<float4*>(op + 16 * db) =
-                make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+            store_f4(op + 16 * db, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
         } else {
           float* po = w.part_o + (slot * w.ncol + hq) * D + 4 * grp;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            *reinterpret_cast<float4*>(po + 16 * db) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
-          if (grp == 0) w.part_ml[slot * w.ncol + hq] = make_float2(m, l);
+            store_f4(po + 16 * db, o[db][0], o[db][1], o[db][2], o[db][3]);
+          if (grp == 0) store_f2(w.part_ml + slot * w.ncol + hq, m, l);
         }
       }
 
