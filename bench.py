@@ -72,7 +72,8 @@ def algorithmic_work(spec, mfma_rows: bool, verify_rows: int = 1):
 
 def measure_ceilings(pk, torch, reps: int = 10):
     """Measured HBM ceilings on this device: streaming copy of 4 GiB (read + write
-    bytes) and a read-only pass over 8 GiB, each the median of `reps` runs."""
+    bytes), a read-only pass over 8 GiB and a gather of its 4 KiB pages in random
+    order, each the median of `reps` runs."""
     dev = "cuda:0"
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
@@ -99,9 +100,15 @@ def measure_ceilings(pk, torch, reps: int = 10):
     out = torch.empty(65536, dtype=torch.int32, device=dev)
     ms = timed(lambda: pk.pa_measure_read(big, out))
     read_gbs = (1 << 33) / (ms * 1e-3) / 1e9
-    del big, out
+    # every 4 KiB page of the same 8 GiB once, in a random order (the decode
+    # step's access pattern: one (block, kv head) page of K or V at a time)
+    page = 4096
+    perm = torch.randperm((1 << 33) // page, generator=torch.Generator().manual_seed(0)).to(torch.int32).to(dev)
+    ms = timed(lambda: pk.pa_measure_gather(big, perm, page, out))
+    gather_gbs = (1 << 33) / (ms * 1e-3) / 1e9
+    del big, out, perm
     torch.cuda.empty_cache()
-    return dict(copy_GBps=copy_gbs, read_GBps=read_gbs)
+    return dict(copy_GBps=copy_gbs, read_GBps=read_gbs, gather4k_GBps=gather_gbs)
 
 
 def recorded_traffic(kernel: str, cfg_id: int):
@@ -357,6 +364,7 @@ def main(argv=None):
         if ceil:
             roof["frac_of_measured_copy"] = ach / ceil["copy_GBps"]
             roof["frac_of_measured_read"] = ach / ceil["read_GBps"]
+            roof["frac_of_measured_gather4k"] = ach / ceil["gather4k_GBps"]
     res = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

@@ -148,8 +148,9 @@ enum {
                                 resident wavefront (VALU kernel) or per wavefront of one
                                 workgroup per CU (MFMA kernel) */
   PA_OPT_DECODE_BUFFERS = 4, /* pages a decode wavefront holds at once (the page being scored
-                                plus the ones in flight): VALU kernel 1 or 2, MFMA kernel 2..4;
-                                0 or a value the kernel does not take: automatic */
+                                plus the ones in flight): VALU kernel 1 or 2, MFMA kernel 2..4
+                                (a decode-only step the MFMA kernel plans itself always holds
+                                2); 0 or a value the kernel does not take: automatic */
   PA_OPT_DECODE_KERNEL = 5,  /* row-wise rows of bf16 steps: 0 automatic (MFMA), 1 VALU kernel,
                                 2 MFMA kernel; float32 steps always take the VALU kernel */
   PA_OPT_VERIFY_ROWS = 6     /* bf16 steps with the MFMA row-wise kernel: a sequence with 2..n

@@ -6,8 +6,8 @@
  * per new token and is bound by memory bandwidth (Inside vLLM summary,
  * techfeed.io, section "エンジンの中核：スケジューラとKVキャッシュ管理"), so
  * the decode kernel is judged against what a plain streaming kernel achieves
- * on the same device: a copy (bytes read + bytes written) and a read-only
- * reduction.
+ * on the same device: a copy (bytes read + bytes written), a read-only
+ * reduction, and a gather of whole pages in random order.
  *
  * Same conventions as pa.h: device pointers, `stream` is a hipStream_t (NULL =
  * null stream), calls only enqueue work, errors are negative pa_status codes
@@ -32,6 +32,18 @@ int pa_measure_copy(void* dst, const void* src, size_t bytes, void* stream);
  * them per workgroup into out (device, at least 65536 uint32 entries), so the
  * reads cannot be elided.  Same size and alignment rules as pa_measure_copy. */
 int pa_measure_read(const void* src, size_t bytes, uint32_t* out, void* stream);
+
+/* Reads npages whole pages of page_bytes bytes each, page pages[i] (device
+ * int32 array) at src + pages[i] * page_bytes, in the given order, and writes
+ * one 32-bit XOR per workgroup into out (at least 65536 uint32 entries).
+ * Page numbers are clamped into [0, src_pages), so nothing outside the
+ * src_pages * page_bytes buffer is read.  With a random permutation of 4 KB
+ * pages this is the access pattern of the decode step (every (block, kv head)
+ * page of K or V is a 4 KB run at a random place in the pool), without its
+ * arithmetic.  page_bytes must be a positive multiple of 1024; src 16-byte
+ * aligned. */
+int pa_measure_gather(const void* src, int64_t src_pages, const int32_t* pages, int64_t npages,
+                      int32_t page_bytes, uint32_t* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -51,6 +51,7 @@ SIGNATURES = {
     "pa_profile_read": (_i32, [C.POINTER(C.c_int64), C.POINTER(C.c_double)]),
     "pa_measure_copy": (_i32, [_vp, _vp, _sz, _vp]),
     "pa_measure_read": (_i32, [_vp, _sz, _vp, _vp]),
+    "pa_measure_gather": (_i32, [_vp, _i64, _vp, _i64, _i32, _vp, _vp]),
     "pa_pool_create": (_vp, [_i64, _i32, _pi32]),
     "pa_pool_destroy": (None, [_vp]),
     "pa_allocate_slots": (_i32, [_vp, _i64, _i64, _i64, _pi32, _i32, _pi32]),
@@ -202,6 +203,19 @@ def pa_measure_read(src, out) -> None:
         raise ValueError("out must hold 65536 32-bit entries")
     _check(lib().pa_measure_read(_dev_ptr(src, "src"), src.numel() * src.element_size(), _dev_ptr(out, "out"),
                                  _stream_handle(src.device)))
+
+
+def pa_measure_gather(src, pages, page_bytes: int, out) -> None:
+    """Reads the page_bytes pages of src named by the int32 device tensor pages, in
+    order; out is an int32 device tensor of >= 65536 entries."""
+    import torch
+    if out.numel() < 65536 or out.dtype.itemsize != 4:
+        raise ValueError("out must hold 65536 32-bit entries")
+    if pages.dtype != torch.int32:
+        raise ValueError("pages must be int32")
+    nb = src.numel() * src.element_size()
+    _check(lib().pa_measure_gather(_dev_ptr(src, "src"), nb // page_bytes, _dev_ptr(pages, "pages"), pages.numel(),
+                                   page_bytes, _dev_ptr(out, "out"), _stream_handle(src.device)))
 
 
 # ----------------------------------------------------------------- host calls

@@ -339,18 +339,22 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
       // done too, the page loop starts with nothing else in flight
       wait_vmcnt<0>();
 
+      // V pages come into registers (the same 1 KB runs per instruction as the
+      // LDS copy would read) and are written to the page's LDS buffer when it
+      // is multiplied: on short ranges (tens of pages) this measured faster
+      // than copying them with global_load_lds
+      u32x4 vreg[NBUF][IPG];
       auto issue = [&](int f, u32x4 (&kf)[KS], auto bufc) __attribute__((always_inline)) {
         if (f > 0 && (f & (kWave - 1)) == 0) table(f);
         const int32_t braw = __builtin_amdgcn_readlane(ids, f & (kWave - 1));
         const int kh = __builtin_amdgcn_readlane(khs, f & (kWave - 1));
         const int32_t b = braw < 0 ? 0 : (braw >= a.nb ? int32_t(a.nb - 1) : braw);  // never leave the pool
         const int64_t pb = (int64_t(b) * hkv + kh) * PAGE;
-        char* dv = vbuf(bufc);
 #pragma unroll
         for (int ii = 0; ii < IPG; ++ii) {
           const int row = ii * RPI + dma_row;
           const int64_t gv = pb + int64_t(row) * RB + 16 * (dma_chunk ^ v_swz<CH>(row));
-          __builtin_amdgcn_global_load_lds(vbase + gv, (lds_void_t*)(dv + ii * RPI * RB), 16, 0, 0);
+          vreg[decltype(bufc)::value][ii] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + gv));
         }
         const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + pb + int64_t(hq) * RB);
 #pragma unroll
@@ -380,6 +384,9 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
           }
         }
         char* vs = vbuf(bufc);
+#pragma unroll
+        for (int ii = 0; ii < IPG; ++ii)
+          *reinterpret_cast<u32x4*>(vs + ii * RPI * RB + 16 * lane) = vreg[decltype(bufc)::value][ii];
         const int pos0 = cp * kBlock;  // first key of the page
         f32x4_t sc = f32x4_t{};
 #pragma unroll
@@ -444,33 +451,56 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
         }
       };
 
-      // stream page f uses LDS buffer and K register set f % 2
-      u32x4 kset[2][KS];
+      // stream page f uses LDS buffer and K register set f % NBUF; pages
+      // f + 1 .. f + NBUF - 1 fly while page f (landed) is multiplied
+      u32x4 kset[NBUF][KS];
       issue(0, kset[0], Buf<0>{});
-      // page f + 1 flies while page f (landed) is multiplied
+      if constexpr (NBUF > 2) {
+        if (1 < total) issue(1, kset[1], Buf<1>{});
+      }
+      if constexpr (NBUF > 3) {
+        if (2 < total) issue(2, kset[2], Buf<2>{});
+      }
+      // a full step: the page NBUF - 1 ahead exists
       auto step = [&](int f, auto bufc) __attribute__((always_inline)) {
         constexpr int B = decltype(bufc)::value;
-        issue(f + 1, kset[1 - B], Buf<1 - B>{});
-        wait_vmcnt<PER_PAGE>();
+        constexpr int BN = (B + NBUF - 1) % NBUF;
+        issue(f + NBUF - 1, kset[BN], Buf<BN>{});
+        wait_vmcnt<(NBUF - 1) * PER_PAGE>();
         compute(kset[B], bufc);
       };
-      // the last page: nothing flies behind it
-      auto last = [&](auto bufc) __attribute__((always_inline)) {
-        wait_vmcnt<0>();
-        compute(kset[decltype(bufc)::value], bufc);
+      // a step near the end of the stream: `later` pages fly behind page f
+      auto tail_step = [&](int f, auto bufc) __attribute__((always_inline)) {
+        constexpr int B = decltype(bufc)::value;
+        constexpr int BN = (B + NBUF - 1) % NBUF;
+        if (f >= total) return;
+        if (f + NBUF - 1 < total) issue(f + NBUF - 1, kset[BN], Buf<BN>{});
+        const int later = min(NBUF - 1, total - 1 - f);
+        if (later >= 3) wait_vmcnt<3 * PER_PAGE>();
+        else if (later == 2) wait_vmcnt<2 * PER_PAGE>();
+        else if (later == 1) wait_vmcnt<PER_PAGE>();
+        else wait_vmcnt<0>();
+        compute(kset[B], bufc);
       };
-      // every pass of the loop runs two full steps (one path through it, so
+      // every pass of the loop runs NBUF full steps (one path through it, so
       // the compiler's own waits for the K registers stay per page)
       int f = 0;
-      for (; f + 2 < total; f += 2) {
+      for (; f + 2 * NBUF - 2 < total; f += NBUF) {
         step(f, Buf<0>{});
         step(f + 1, Buf<1>{});
+        if constexpr (NBUF > 2) step(f + 2, Buf<2 % NBUF>{});
+        if constexpr (NBUF > 3) step(f + 3, Buf<3 % NBUF>{});
       }
-      if (f + 1 < total) {
-        step(f, Buf<0>{});
-        last(Buf<1>{});
-      } else {
-        last(Buf<0>{});
+      // at most 2 * NBUF - 2 pages are left
+      tail_step(f, Buf<0>{});
+      tail_step(f + 1, Buf<1 % NBUF>{});
+      tail_step(f + 2, Buf<2 % NBUF>{});
+      if constexpr (NBUF > 2) {
+        tail_step(f + 3, Buf<3 % NBUF>{});
+      }
+      if constexpr (NBUF > 3) {
+        tail_step(f + 4, Buf<4 % NBUF>{});
+        tail_step(f + 5, Buf<5 % NBUF>{});
       }
     }
   };

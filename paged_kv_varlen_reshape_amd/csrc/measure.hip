@@ -1,4 +1,5 @@
-// Ceiling kernels: streaming copy and read-only reduction over HBM.
+// Ceiling kernels: streaming copy, read-only reduction and random page gather
+// over HBM.
 //
 // A grid of a few workgroups per CU walks the buffer with 16-byte lanes, each
 // thread keeping four independent loads in flight per iteration, so the
@@ -54,6 +55,48 @@ read_kernel(const u32x4* __restrict__ src, int64_t n, uint32_t* __restrict__ out
   }
 }
 
+// Random page gather: one wavefront reads kGatherPages whole pages at a time
+// (page_bytes / 1024 16-byte loads per lane and page), the page numbers taken
+// from `pages` in order, clamped into the buffer.
+constexpr int kGatherPages = 4;
+
+__global__ void __launch_bounds__(kMeasureThreads)
+gather_kernel(const char* __restrict__ src, const int32_t* __restrict__ pages, int64_t npages, int64_t src_pages,
+              int32_t page_bytes, uint32_t* __restrict__ out) {
+  __shared__ uint32_t s[kMeasureThreads / kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t waves = int64_t(gridDim.x) * (kMeasureThreads / kWave);
+  const int per_lane = page_bytes / (kWave * 16);  // 16-byte loads per lane and page
+  uint32_t acc = 0;
+  for (int64_t p0 = (int64_t(blockIdx.x) * (kMeasureThreads / kWave) + threadIdx.x / kWave) * kGatherPages;
+       p0 < npages; p0 += waves * kGatherPages) {
+    const u32x4* base[kGatherPages];
+#pragma unroll
+    for (int k = 0; k < kGatherPages; ++k) {
+      int64_t pg = p0 + k < npages ? pages[p0 + k] : 0;
+      pg = pg < 0 ? 0 : (pg >= src_pages ? src_pages - 1 : pg);
+      base[k] = reinterpret_cast<const u32x4*>(src + pg * page_bytes);
+    }
+    for (int j = 0; j < per_lane; ++j) {
+      u32x4 v[kGatherPages];
+#pragma unroll
+      for (int k = 0; k < kGatherPages; ++k)
+        v[k] = p0 + k < npages ? __builtin_nontemporal_load(base[k] + j * kWave + lane) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int k = 0; k < kGatherPages; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) acc ^= __shfl_xor(acc, d);
+  if (lane == 0) s[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int ww = 0; ww < kMeasureThreads / kWave; ++ww) t ^= s[ww];
+    out[blockIdx.x] = t;
+  }
+}
+
 int measure_grid() {
   const int g = device_cus() * 8;
   return g < 65536 ? g : 65536;
@@ -91,4 +134,18 @@ extern "C" int pa_measure_read(const void* src, size_t bytes, uint32_t* out, voi
                      static_cast<const u32x4*>(src), int64_t(bytes / 16), out);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : fail(PA_ERR_HIP, "pa_measure_read: launch failed: %s", hipGetErrorString(e));
+}
+
+extern "C" int pa_measure_gather(const void* src, int64_t src_pages, const int32_t* pages, int64_t npages,
+                                 int32_t page_bytes, uint32_t* out, void* stream) {
+  clear_error();
+  if (int rc = check(src, out, 16, "pa_measure_gather")) return rc;
+  if (!pages || npages <= 0 || src_pages <= 0)
+    return fail(PA_ERR_INVALID, "pa_measure_gather: empty page list or buffer");
+  if (page_bytes <= 0 || page_bytes % (kWave * 16) != 0)
+    return fail(PA_ERR_INVALID, "pa_measure_gather: page_bytes must be a positive multiple of 1024");
+  hipLaunchKernelGGL(gather_kernel, dim3(measure_grid()), dim3(kMeasureThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const char*>(src), pages, npages, src_pages, page_bytes, out);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : fail(PA_ERR_HIP, "pa_measure_gather: launch failed: %s", hipGetErrorString(e));
 }

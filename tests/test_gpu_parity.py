@@ -129,6 +129,36 @@ def test_bf16_decode_kernels_match_oracle(seed, kernel, nbuf):
             _check_attention(spec, ds, ds.attention())
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_self_planned_decode_ranges(seed):
+    """Decode-only bf16 steps small enough for the MFMA decode kernel to plan
+    itself: contexts from 0 (one-page pairs) to a few thousand tokens, ranges from
+    one page (every pair cut) to 512 pages (a range over many pairs, and over more
+    than 64 pages of one pair), two to four pages in flight per wavefront, every
+    group size and both head sizes."""
+    import math
+    r = np.random.default_rng((seed, 7))
+    g = [1, 2, 4, 8][seed % 4]
+    hkv = [2, 1][(seed // 4) % 2]
+    d = [64, 128][(seed // 2) % 2]
+    n = int(r.integers(20, 120))
+    ctx = np.where(r.random(n) < 0.4, r.integers(0, 40, n), r.integers(40, 3000, n))
+    reqs = [W.Request(i, int(c), 1) for i, c in enumerate(ctx)]
+    nb = sum(-(-(int(c) + 1) // 16) for c in ctx) + 4
+    order = np.random.default_rng((seed, 8)).permutation(nb).astype(np.int32)
+    spec = W.StepSpec("self-planned decode", 3000 + seed, hkv * g, hkv, d, "bf16", 16, nb, 1.0 / math.sqrt(d),
+                      reqs, initial_order=order, table_rows=2048, seed=3000 + seed)
+    print(f"self-planned decode seed={seed} g={g} hkv={hkv} d={d} seqs={n}", flush=True)
+    ds = build_device_step(spec)
+    ds.reshape()
+    assert ds.max_query_len == 1
+    for nbuf in (2, 3, 4):  # pages in flight per wavefront
+        pk.pa_set_option(pk.PA_OPT_DECODE_BUFFERS, nbuf)
+        for split in (0, 16, 256, 1024, 8192):
+            pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, split)
+            _check_attention(spec, ds, ds.attention())
+
+
 def test_many_sequences_plan_fallbacks():
     """More sequences than the plan keeps in registers and more rows than its
     LDS range search holds: both fallback paths, checked on sampled sequences."""
