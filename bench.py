@@ -71,9 +71,9 @@ def algorithmic_work(spec, mfma_rows: bool, verify_rows: int = 1):
 
 
 def measure_ceilings(pk, torch, reps: int = 10):
-    """Measured HBM ceilings on this device: streaming copy of 4 GiB (read + write
-    bytes), a read-only pass over 8 GiB and a gather of its 4 KiB pages in random
-    order, each the median of `reps` runs."""
+    """Measured ceilings on this device: streaming copy of 4 GiB (read + write
+    bytes), a read-only pass over 8 GiB, a gather of its 4 KiB pages in random
+    order, and a bf16 matrix-core loop, each the median of `reps` runs."""
     dev = "cuda:0"
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
@@ -106,9 +106,15 @@ def measure_ceilings(pk, torch, reps: int = 10):
     perm = torch.randperm((1 << 33) // page, generator=torch.Generator().manual_seed(0)).to(torch.int32).to(dev)
     ms = timed(lambda: pk.pa_measure_gather(big, perm, page, out))
     gather_gbs = (1 << 33) / (ms * 1e-3) / 1e9
-    del big, out, perm
+    del big, perm
+    # bf16 matrix cores: a register-only loop of 32x32x16 products on every CU
+    outf = out.view(torch.float32)
+    flops = pk.pa_measure_mfma(40000, outf)
+    ms = timed(lambda: pk.pa_measure_mfma(40000, outf))
+    mfma_tflops = flops / (ms * 1e-3) / 1e12
+    del out, outf
     torch.cuda.empty_cache()
-    return dict(copy_GBps=copy_gbs, read_GBps=read_gbs, gather4k_GBps=gather_gbs)
+    return dict(copy_GBps=copy_gbs, read_GBps=read_gbs, gather4k_GBps=gather_gbs, mfma_bf16_TFLOPs=mfma_tflops)
 
 
 def recorded_traffic(kernel: str, cfg_id: int):
@@ -356,6 +362,8 @@ def main(argv=None):
                     frac=ach / MFMA_BF16_PEAK_TFLOPS, traffic=recorded_traffic("chunk_mfma", spec.cfg_id),
                     kernel="chunk_mfma", algorithmic_flops=work["chunk_flops"],
                     kernel_avg_us=chunk_avg * 1e3)
+        if ceil:
+            roof["frac_of_measured_mfma"] = ach / ceil["mfma_bf16_TFLOPs"]
     else:
         ach = work["decode_kernel_bytes"] / (decode_avg * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS,

@@ -7,7 +7,8 @@
  * techfeed.io, section "エンジンの中核：スケジューラとKVキャッシュ管理"), so
  * the decode kernel is judged against what a plain streaming kernel achieves
  * on the same device: a copy (bytes read + bytes written), a read-only
- * reduction, and a gather of whole pages in random order.
+ * reduction, and a gather of whole pages in random order.  The chunk kernel
+ * is compute-bound and is judged against a matrix-core loop.
  *
  * Same conventions as pa.h: device pointers, `stream` is a hipStream_t (NULL =
  * null stream), calls only enqueue work, errors are negative pa_status codes
@@ -44,6 +45,14 @@ int pa_measure_read(const void* src, size_t bytes, uint32_t* out, void* stream);
  * aligned. */
 int pa_measure_gather(const void* src, int64_t src_pages, const int32_t* pages, int64_t npages,
                       int32_t page_bytes, uint32_t* out, void* stream);
+
+/* bf16 matrix-core ceiling: two workgroups of four wavefronts per CU, each
+ * wavefront running `iters` rounds of four independent 32x32x16 bf16 products
+ * (v_mfma_f32_32x32x16_bf16) on register operands with no memory traffic; the
+ * chunk kernel's products are these.  Writes one float per wavefront into out
+ * (device, at least 65536 entries) and the launch's flop count (2 per
+ * multiply-add) into *flops (host).  iters must be positive. */
+int pa_measure_mfma(int32_t iters, float* out, int64_t* flops, void* stream);
 
 #ifdef __cplusplus
 }

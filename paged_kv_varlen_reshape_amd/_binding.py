@@ -52,6 +52,7 @@ SIGNATURES = {
     "pa_measure_copy": (_i32, [_vp, _vp, _sz, _vp]),
     "pa_measure_read": (_i32, [_vp, _sz, _vp, _vp]),
     "pa_measure_gather": (_i32, [_vp, _i64, _vp, _i64, _i32, _vp, _vp]),
+    "pa_measure_mfma": (_i32, [_i32, _vp, C.POINTER(C.c_int64), _vp]),
     "pa_pool_create": (_vp, [_i64, _i32, _pi32]),
     "pa_pool_destroy": (None, [_vp]),
     "pa_allocate_slots": (_i32, [_vp, _i64, _i64, _i64, _pi32, _i32, _pi32]),
@@ -216,6 +217,16 @@ def pa_measure_gather(src, pages, page_bytes: int, out) -> None:
     nb = src.numel() * src.element_size()
     _check(lib().pa_measure_gather(_dev_ptr(src, "src"), nb // page_bytes, _dev_ptr(pages, "pages"), pages.numel(),
                                    page_bytes, _dev_ptr(out, "out"), _stream_handle(src.device)))
+
+
+def pa_measure_mfma(iters: int, out) -> int:
+    """bf16 matrix-core loop; out is a float32 device tensor of >= 65536 entries.
+    Returns the launch's flop count."""
+    if out.numel() < 65536 or out.dtype.itemsize != 4:
+        raise ValueError("out must hold 65536 32-bit entries")
+    flops = C.c_int64(0)
+    _check(lib().pa_measure_mfma(int(iters), _dev_ptr(out, "out"), C.byref(flops), _stream_handle(out.device)))
+    return flops.value
 
 
 # ----------------------------------------------------------------- host calls

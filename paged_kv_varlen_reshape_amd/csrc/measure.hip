@@ -1,5 +1,5 @@
 // Ceiling kernels: streaming copy, read-only reduction and random page gather
-// over HBM.
+// over HBM, and a bf16 matrix-core loop.
 //
 // A grid of a few workgroups per CU walks the buffer with 16-byte lanes, each
 // thread keeping four independent loads in flight per iteration, so the
@@ -97,6 +97,37 @@ gather_kernel(const char* __restrict__ src, const int32_t* __restrict__ pages, i
   }
 }
 
+// Matrix-core ceiling: every wavefront runs `iters` rounds of kMfmaChains
+// independent v_mfma_f32_32x32x16_bf16 products on register operands (no
+// memory inside the loop), two workgroups of four wavefronts per CU.
+constexpr int kMfmaChains = 4;
+constexpr int kMfmaWgPerCu = 2;
+typedef __bf16 mbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float mf32x16_t __attribute__((ext_vector_type(16)));
+
+__global__ void __launch_bounds__(kMeasureThreads)
+mfma_kernel(int32_t iters, float* __restrict__ out) {
+  // finite, thread-dependent bf16 operands (exponents near 1) so nothing folds
+  const uint32_t t = (threadIdx.x + 7u * blockIdx.x) & 0x7fu;
+  const uint32_t w0 = 0x3f803f80u | (t << 16) | t;
+  const u32x4 av = {w0, w0 ^ 0x10001u, w0 ^ 0x20002u, w0 ^ 0x30003u};
+  const u32x4 bv = {w0 ^ 0x40004u, w0 ^ 0x50005u, w0, w0 ^ 0x60006u};
+  const mbf16x8_t a = __builtin_bit_cast(mbf16x8_t, av), b = __builtin_bit_cast(mbf16x8_t, bv);
+  mf32x16_t acc[kMfmaChains];
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c) acc[c] = mf32x16_t{};
+  for (int32_t i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < kMfmaChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += acc[c][j];
+  if ((threadIdx.x & (kWave - 1)) == 0) out[blockIdx.x * (kMeasureThreads / kWave) + threadIdx.x / kWave] = s;
+}
+
 int measure_grid() {
   const int g = device_cus() * 8;
   return g < 65536 ? g : 65536;
@@ -148,4 +179,17 @@ extern "C" int pa_measure_gather(const void* src, int64_t src_pages, const int32
                      static_cast<const char*>(src), pages, npages, src_pages, page_bytes, out);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : fail(PA_ERR_HIP, "pa_measure_gather: launch failed: %s", hipGetErrorString(e));
+}
+
+extern "C" int pa_measure_mfma(int32_t iters, float* out, int64_t* flops, void* stream) {
+  clear_error();
+  if (!out || !flops) return fail(PA_ERR_INVALID, "pa_measure_mfma: null pointer");
+  if (iters <= 0) return fail(PA_ERR_INVALID, "pa_measure_mfma: iters must be positive");
+  const int grid = device_cus() * kMfmaWgPerCu;
+  if (int64_t(grid) * (kMeasureThreads / kWave) > 65536)
+    return fail(PA_ERR_UNSUPPORTED, "pa_measure_mfma: too many compute units for the output buffer");
+  *flops = int64_t(grid) * (kMeasureThreads / kWave) * iters * kMfmaChains * (2ll * 32 * 32 * 16);
+  hipLaunchKernelGGL(mfma_kernel, dim3(grid), dim3(kMeasureThreads), 0, static_cast<hipStream_t>(stream), iters, out);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : fail(PA_ERR_HIP, "pa_measure_mfma: launch failed: %s", hipGetErrorString(e));
 }

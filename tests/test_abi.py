@@ -46,6 +46,9 @@ def test_measure_rejects_bad_arguments():
     assert lib.pa_measure_gather(16, 4, 32, 4, 1000, 4096, None) == pk.PA_ERR_INVALID  # page not 1 KiB-aligned
     assert lib.pa_measure_gather(16, 4, None, 4, 4096, 4096, None) == pk.PA_ERR_INVALID
     assert lib.pa_measure_gather(16, 0, 32, 4, 4096, 4096, None) == pk.PA_ERR_INVALID
+    flops = ctypes.c_int64(0)
+    assert lib.pa_measure_mfma(0, 4096, ctypes.byref(flops), None) == pk.PA_ERR_INVALID
+    assert lib.pa_measure_mfma(10, None, ctypes.byref(flops), None) == pk.PA_ERR_INVALID
 
 
 def test_reshape_rejects_bad_arguments():
