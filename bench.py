@@ -333,6 +333,15 @@ def main(argv=None):
     torch.cuda.synchronize()
     prof = pk.pa_profile_read()
     pk.pa_profile_enable(0)
+    # third pass: HIP events around each whole step, for its spread (p10 / median / p90)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        run(args.warmup + i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    pct = lambda q: step_us[min(len(step_us) - 1, int(q * (len(step_us) - 1) + 0.5))]
 
     use_mfma = spec.dtype == "bf16" and pk.pa_get_option(pk.PA_OPT_FORCE_ROWWISE) == 0 and prof["chunk_mfma"][0] > 0
     g = spec.num_q_heads // spec.num_kv_heads
@@ -382,6 +391,7 @@ def main(argv=None):
                    "causal_flops": work["causal_flops"], "replicas": reps},
         "roofline": roof,
         "kernels_avg_us": {k: (v[1] / v[0] * 1e3 if v[0] else None) for k, v in prof.items()},
+        "step_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
         "launch": "hip_graph" if args.graph else "stream",
         "ceilings": ceil,
     }
