@@ -105,10 +105,13 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t
  *   context_lens     [num_seqs] int32, cached tokens before this step
  *   out              [num_tokens, num_q_heads, head_dim] float32
  *   max_query_len    (host) the longest query of the step, as a scheduler
- *                    knows it; only <= 1 versus > 1 is used: <= 1 routes every
- *                    row to the row-wise kernel and skips the chunk kernel's
- *                    launch.  A wrong value changes which kernel computes a
- *                    row, never the result; pass num_tokens if unknown
+ *                    knows it.  <= 1 routes every row to the row-wise kernel
+ *                    and skips the chunk kernel's launch; > 1 with
+ *                    num_tokens == num_seqs * max_query_len (every sequence
+ *                    that long) routes every row to the chunk kernel and skips
+ *                    the row-wise kernels' launches.  A wrong value changes
+ *                    which kernel computes a row, never the result; pass
+ *                    num_tokens if unknown
  *   workspace        device buffer of at least
  *                    pa_attention_workspace_size(...) bytes, 256-B aligned
  * The new K/V of the step must already be in the caches (call

@@ -226,6 +226,13 @@ extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_ca
   // has the per-column causal limits (and the debug route keeps one row per record)
   pa_args.verify_rows =
       bf16 && max_query_len > 1 && decode_uses_mfma(1) && !option(PA_OPT_FORCE_ROWWISE) ? verify_rows(group) : 1;
+  // T = S * max_query_len: with a true hint every sequence has max_query_len rows, too many
+  // for a row-wise record, so no row-wise row exists and the decode and merge kernels are not
+  // launched.  The plan then sends every sequence to the chunk kernel, so a wrong hint (some
+  // sequences shorter, others longer) still gets every row computed.
+  const bool all_chunk = use_mfma && num_seqs > 0 && max_query_len > pa_args.verify_rows &&
+                         int64_t(num_seqs) * max_query_len == num_tokens;
+  pa_args.all_chunk = all_chunk ? 1 : 0;
 
   AttnArgs a{};
   a.q = q;
@@ -263,11 +270,11 @@ extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_ca
     KernelTimer t(PA_K_CHUNK, st);
     e = launch_chunk(a, w, group, st);
   }
-  if (e == hipSuccess) {
+  if (e == hipSuccess && !all_chunk) {
     KernelTimer t(PA_K_DECODE, st);
     e = launch_decode(a, w, group, st);
   }
-  if (e == hipSuccess) {
+  if (e == hipSuccess && !all_chunk) {
     KernelTimer t(PA_K_MERGE, st);
     // automatic ranges number at most num_ranges; fixed-length ones up to the capacity
     e = launch_merge(a, w, group, pa_args.fixed_units > 0 ? w.ranges_cap : pa_args.num_ranges, st);

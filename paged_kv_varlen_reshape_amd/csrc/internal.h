@@ -91,6 +91,8 @@ struct PlanArgs {
   int32_t tile_rows;      // query rows per chunk-kernel tile
   int32_t verify_rows;    // >1: sequences with 2..verify_rows query rows become one row-wise
                           //   record (their rows share the K/V pages); 1: one record per row
+  int32_t all_chunk;      // 1: every sequence with query rows goes to the chunk kernel (the step
+                          //   launches no row-wise kernel)
 };
 hipError_t launch_plan(const PlanArgs& a, const Workspace& w, hipStream_t st);
 

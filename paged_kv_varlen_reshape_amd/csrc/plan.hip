@@ -83,8 +83,8 @@ __device__ __forceinline__ SeqInfo seq_info(const PlanArgs& a, int64_t i, bool v
   if (!valid || r0 < 0 || r0 >= a.num_tokens) q = 0;
   c = max(c, 0);
   if (int64_t(c) + q > a.max_len) q = c >= a.max_len ? 0 : a.max_len - c;
-  const bool group = q > 1 && q <= a.verify_rows;
-  return SeqInfo{r0, q, c, !group && q > 1 && a.use_mfma, group};
+  const bool group = !a.all_chunk && q > 1 && q <= a.verify_rows;
+  return SeqInfo{r0, q, c, !group && q > (a.all_chunk ? 0 : 1) && a.use_mfma, group};
 }
 
 __device__ __forceinline__ void seq_counts(const SeqInfo& s, int tile_rows, int64_t hkv, int64_t& ntile,

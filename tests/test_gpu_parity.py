@@ -198,7 +198,8 @@ def test_short_queries_share_pages(seed):
 
 def test_max_query_len_hint_never_changes_results():
     """<= 1 sends every row to the row-wise kernel: exact for a decode step,
-    within tolerance (other kernel) for a mixed step given a wrong hint."""
+    within tolerance (other kernel) for a mixed step given a wrong hint; a hint
+    with T = S * hint sends every row to the chunk kernel, right or wrong."""
     dec = build_device_step(W.make_config(2))
     dec.reshape()
     a = dec.attention().clone()
@@ -213,6 +214,23 @@ def test_max_query_len_hint_never_changes_results():
     out = pk.pa_attention(mix.q, mix.k_cache, mix.v_cache, mix.block_tables, mix.seq_lens, mix.query_start_loc,
                           mix.context_lens, spec.scale, max_query_len=1)
     _check_attention(spec, mix, out)
+    # T = S * hint sends every row to the chunk kernel; a wrong hint of that kind (a
+    # one-row sequence next to longer ones) must still get every row computed
+    import math
+    for d, g in ((128, 4), (64, 8), (128, 1)):
+        reqs = [W.Request(i, c, q) for i, (c, q) in enumerate([(40, 1), (300, 5), (0, 1), (17, 5), (1000, 3),
+                                                                 (5, 3)])]
+        nb = sum(-(-(r.context + r.query) // 16) for r in reqs) + 4
+        order = np.random.default_rng(d + g).permutation(nb).astype(np.int32)
+        sp = W.StepSpec("wrong hint", 4000 + d + g, 2 * g, 2, d, "bf16", 16, nb, 1.0 / math.sqrt(d), reqs,
+                        initial_order=order, table_rows=2048, seed=4000 + d + g)
+        ds = build_device_step(sp)
+        ds.reshape()
+        assert ds.q.shape[0] == 6 * 3 and ds.max_query_len == 5
+        for hint in (3, 5):  # 3: every row to the chunk kernel (T = 6 * 3); 5: the usual routing
+            out = pk.pa_attention(ds.q, ds.k_cache, ds.v_cache, ds.block_tables, ds.seq_lens, ds.query_start_loc,
+                                  ds.context_lens, sp.scale, max_query_len=hint)
+            _check_attention(sp, ds, out)
 
 
 def test_forced_rowwise_and_split_sizes_agree():
