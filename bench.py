@@ -267,7 +267,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the step shards by sequence or kv head with no exchange; see DESIGN.md)", file=sys.stderr)
         return 2
 
