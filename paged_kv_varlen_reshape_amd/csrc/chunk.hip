@@ -23,7 +23,7 @@
 // holds, and V^T is read in the same key order.
 //
 // Staging is DMA: wavefront w copies page w of the tile (16 rows of K and of
-// V) from the pool into LDS with global_load_lds_dwordx4 (one wave-uniform
+// V) from the pool into LDS with buffer_load_dwordx4 ... lds (one wave-uniform
 // block id, each instruction fills 1 KiB of LDS in lane order), so K and V
 // never pass through registers.  K is read back as the MFMA A operand with
 // ds_read_b128; V stays row-major and ds_read_b64_tr_b16 returns it
@@ -69,15 +69,42 @@ constexpr int kThreads = 256;
 constexpr int kHandoverTiles = 4;  // the next item is claimed this many key tiles before the end
 
 typedef const __attribute__((address_space(4))) int32_t const_i32;  // read with scalar loads
-constexpr int KLOOK = 2;  // K operand reads in flight ahead of the Q.K products
-
-// instruction classes of __builtin_amdgcn_sched_group_barrier
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
+constexpr int KLOOK = 3;  // k-steps of K operand reads in flight ahead of the Q.K products
+constexpr int VLOOK = 4;  // V^T operand reads in flight ahead of the P.V products
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x of lanes l and l ^ 32 (v_permlane32_swap of x with itself: a VALU exchange of
+// the two lane halves; in every lane one result holds x of lane l, the other
+// x of lane l ^ 32)
+__device__ __forceinline__ void lane_pair(float x, float& a, float& b) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  a = __builtin_bit_cast(float, uint32_t(sw[0]));
+  b = __builtin_bit_cast(float, uint32_t(sw[1]));
+}
+__device__ __forceinline__ float pair_max(float x) {
+  float a, b;
+  lane_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float a, b;
+  lane_pair(x, a, b);
+  return a + b;
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Raw buffer descriptor over one page (bytes [0, bytes) from base; word 3 =
+// 32-bit data format, the gfx9-family value for untyped byte-offset access).
+// The tile copies go through MUBUF loads into LDS rather than the FLAT-encoded
+// global form: a FLAT load that may write LDS makes the compiler wait for
+// every LDS read with lgkmcnt(0), so no operand read could stay in flight
+// past the one a product needs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const char* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, bytes, 0x00020000);
+}
 
 // two floats -> two bf16 (round to nearest even) in one dword
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -271,13 +298,15 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
       raw = __builtin_amdgcn_readfirstlane(raw);
       const int32_t blk = raw < 0 ? 0 : (raw >= a.nb ? int32_t(a.nb - 1) : raw);  // never leave the pool
       const int64_t page = (int64_t(blk) * a.hkv + kvh) * page_stride;
-      const char* kp = kbase + page;
-      const char* vp = vbase + page;
+      // one buffer descriptor per page: the per-lane offsets stay 32-bit and
+      // a copy can never read past the page
+      const __amdgpu_buffer_rsrc_t rk = page_rsrc(kbase + page, int(page_stride));
+      const __amdgpu_buffer_rsrc_t rv = page_rsrc(vbase + page, int(page_stride));
 #pragma unroll
       for (int j = 0; j < IPG; ++j) {
         const int lrow = wave * kBlock + j * RPI;  // first LDS row of this instruction
-        __builtin_amdgcn_global_load_lds(kp + off_k[j], (lds_void_t*)(dk + lrow * RB), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vp + off_v[j], (lds_void_t*)(dv + lrow * RB), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(dk + lrow * RB), 16, off_k[j], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dv + lrow * RB), 16, off_v[j], 0, 0, 0);
       }
     };
     // after the DMA has landed: V rows of keys at or past kv_end become zeros
@@ -315,31 +344,57 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
       const char* vs = buf ? s_v1 : s_v0;
       const int key0 = kt * kBN;
 
-      // S^T = K Q^T: two 32-key blocks, the chains interleaved.  The products
-      // run at raised wave priority, so the matrix core is fed before the other
-      // wavefront's softmax when both are ready to issue
+      // S^T = K Q^T: two 32-key blocks, the chains interleaved.  The K operand
+      // reads run KLOOK k-steps ahead of the products; sched_barrier pins that
+      // order, so each product waits only for its own reads (counted waits)
+      // instead of for every read in flight.  The products run at raised wave
+      // priority, so the matrix core is fed before the other wavefront's
+      // softmax when both are ready to issue
       __builtin_amdgcn_s_setprio(1);
       f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
       {
         const char* kr = ks + col * RB;
+        u32x4 ka[KSTEPS], kb[KSTEPS];
+        auto kread = [&](int kk) __attribute__((always_inline)) {
+          const int off = 16 * ((2 * kk) ^ kx);
+          ka[kk] = *reinterpret_cast<const u32x4*>(kr + off);
+          kb[kk] = *reinterpret_cast<const u32x4*>(kr + 32 * RB + off);
+        };
+#pragma unroll
+        for (int kk = 0; kk < KLOOK; ++kk) kread(kk);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-          const int off = 16 * ((2 * kk) ^ kx);
-          const u32x4 k0 = *reinterpret_cast<const u32x4*>(kr + off);
-          const u32x4 k1 = *reinterpret_cast<const u32x4*>(kr + 32 * RB + off);
-          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), as_bf16x8(qf[kk]), s[0], 0, 0, 0);
-          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), as_bf16x8(qf[kk]), s[1], 0, 0, 0);
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[kk]), as_bf16x8(qf[kk]), s[0], 0, 0, 0);
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kb[kk]), as_bf16x8(qf[kk]), s[1], 0, 0, 0);
+          if (kk + KLOOK < KSTEPS) kread(kk + KLOOK);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        // schedule: the operand reads run KLOOK steps ahead of the products
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * KLOOK, 0);
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS - KLOOK; ++kk) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * KLOOK, 0);
       }
+
+      // O^T += V^T P^T runs as NPV products, i = t*DBLK + db: 16-key step t
+      // uses accumulator rows j = (t%2)*8 .. +8 of block t/2, i.e. keys
+      // 16t + (i/4)*8 + lg*4 + i%4, loaded as two transposed quarters (i = 0..3:
+      // rows 16t + 4lg + k, i = 4..7: rows 16t + 8 + 4lg + k).  The V^T operands
+      // do not depend on P: the first VLOOK are read now, so their LDS latency
+      // hides behind the softmax, and the rest run VLOOK products ahead
+      constexpr int NPV = 4 * DBLK;
+      u32x4 va[NPV];
+      auto vread = [&](int i) __attribute__((always_inline)) {
+        const int t = i / DBLK, db = i % DBLK;
+        const char* vr = vs + vaddr[db] + 16 * t * RB;
+        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vr));
+        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vr + 8 * RB));
+        va[i] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1)),
+                      __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3)),
+                      __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1)),
+                      __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3))};
+      };
+#pragma unroll
+      for (int i = 0; i < VLOOK; ++i) vread(i);
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
+
       // causal mask (also hides keys past the tile's end): key > pos -> -inf;
       // accumulator row j of block mb is key key0 + lg*4 + mb*32 + (j/4)*8 + j%4
       if constexpr (decltype(masked)::value) {
@@ -353,11 +408,13 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
       // online softmax for this lane's row in the log2 domain.  The reference
       // maximum m only moves when a row's maximum exceeds it by more than 2^8
       // (lazy rescale): weights stay <= 2^8, exact in fp32 and bf16 range, and
-      // the final division by l cancels the common factor.
+      // the final division by l cancels the common factor.  The two lane halves
+      // hold disjoint keys of the same row: they exchange maxima by a VALU lane
+      // swap, which does not queue behind the V^T reads in flight
       float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
       for (int j = 1; j < 16; ++j) mx = fmaxf(fmaxf(mx, s[0][j]), s[1][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+      mx = pair_max(mx) * a.scale_log2;
       // wave-uniform branch (rarely taken after the first tiles); lanes whose
       // maximum did not grow scale by 1
       const bool grow = mx > m + 8.f;
@@ -382,27 +439,17 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
           pk[mb][i] = pack_bf16(p0, p1);
           l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[mb][i]), kOnes, l, false);
         }
+      __builtin_amdgcn_sched_barrier(0);
 
-      // O^T += V^T P^T: four 16-key steps; step t uses accumulator rows
-      // j = (t%2)*8 .. +8 of block t/2, i.e. keys 16t + (i/4)*8 + lg*4 + i%4,
-      // loaded as two transposed quarters (i = 0..3: rows 16t + 4lg + k,
-      // i = 4..7: rows 16t + 8 + 4lg + k)
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int i = 0; i < NPV; ++i) {
+        const int t = i / DBLK, db = i % DBLK;
         const u32x4 pb = {pk[t / 2][(t % 2) * 4 + 0], pk[t / 2][(t % 2) * 4 + 1], pk[t / 2][(t % 2) * 4 + 2],
                           pk[t / 2][(t % 2) * 4 + 3]};
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const char* vr = vs + vaddr[db] + 16 * t * RB;
-          const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vr));
-          const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vr + 8 * RB));
-          const u32x4 va = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1)),
-                            __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3)),
-                            __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1)),
-                            __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3))};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb), o[db], 0, 0, 0);
-        }
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[i]), as_bf16x8(pb), o[db], 0, 0, 0);
+        if (i + VLOOK < NPV) vread(i + VLOOK);
+        __builtin_amdgcn_sched_barrier(0);
       }
 
       __builtin_amdgcn_s_setprio(0);
@@ -428,7 +475,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
     run(max(n_full, 0), n_kt, std::true_type{});
 
     // the two lane halves hold disjoint keys of the same row
-    l += __shfl_xor(l, 32);
+    l = pair_sum(l);
     if (valid) {
       const float inv = 1.f / l;
       float* op = a.out + ((int64_t(r0) + t0 + tt) * a.hq + head) * D;
