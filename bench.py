@@ -112,9 +112,15 @@ def measure_ceilings(pk, torch, reps: int = 10):
     flops = pk.pa_measure_mfma(40000, outf)
     ms = timed(lambda: pk.pa_measure_mfma(40000, outf))
     mfma_tflops = flops / (ms * 1e-3) / 1e12
+    # the same loop on N(0,1)-like operands that change with every product: the
+    # products' power, and the clock the chip holds under them, depend on the data
+    flops = pk.pa_measure_mfma_random(40000, outf)
+    ms = timed(lambda: pk.pa_measure_mfma_random(40000, outf))
+    mfma_random_tflops = flops / (ms * 1e-3) / 1e12
     del out, outf
     torch.cuda.empty_cache()
-    return dict(copy_GBps=copy_gbs, read_GBps=read_gbs, gather4k_GBps=gather_gbs, mfma_bf16_TFLOPs=mfma_tflops)
+    return dict(copy_GBps=copy_gbs, read_GBps=read_gbs, gather4k_GBps=gather_gbs, mfma_bf16_TFLOPs=mfma_tflops,
+                mfma_bf16_random_TFLOPs=mfma_random_tflops)
 
 
 def recorded_traffic(kernel: str, cfg_id: int):
@@ -373,6 +379,7 @@ def main(argv=None):
                     kernel_avg_us=chunk_avg * 1e3)
         if ceil:
             roof["frac_of_measured_mfma"] = ach / ceil["mfma_bf16_TFLOPs"]
+            roof["frac_of_measured_mfma_random"] = ach / ceil["mfma_bf16_random_TFLOPs"]
     else:
         ach = work["decode_kernel_bytes"] / (decode_avg * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS,

@@ -54,6 +54,14 @@ int pa_measure_gather(const void* src, int64_t src_pages, const int32_t* pages, 
  * multiply-add) into *flops (host).  iters must be positive. */
 int pa_measure_mfma(int32_t iters, float* out, int64_t* flops, void* stream);
 
+/* The same matrix-core loop on operands spread like N(0,1) data (random sign,
+ * exponent 2^-3 .. 2^0 and mantissa per bf16 element, four operand sets per
+ * lane taken in turn so every product sees new inputs).  The products' power,
+ * and with it the clock the chip holds, depends on how much their inputs
+ * toggle; the chunk kernel multiplies such data.  Same outputs as
+ * pa_measure_mfma; iters must be a positive multiple of 4. */
+int pa_measure_mfma_random(int32_t iters, float* out, int64_t* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

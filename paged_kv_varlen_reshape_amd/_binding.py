@@ -53,6 +53,7 @@ SIGNATURES = {
     "pa_measure_read": (_i32, [_vp, _sz, _vp, _vp]),
     "pa_measure_gather": (_i32, [_vp, _i64, _vp, _i64, _i32, _vp, _vp]),
     "pa_measure_mfma": (_i32, [_i32, _vp, C.POINTER(C.c_int64), _vp]),
+    "pa_measure_mfma_random": (_i32, [_i32, _vp, C.POINTER(C.c_int64), _vp]),
     "pa_pool_create": (_vp, [_i64, _i32, _pi32]),
     "pa_pool_destroy": (None, [_vp]),
     "pa_allocate_slots": (_i32, [_vp, _i64, _i64, _i64, _pi32, _i32, _pi32]),
@@ -226,6 +227,17 @@ def pa_measure_mfma(iters: int, out) -> int:
         raise ValueError("out must hold 65536 32-bit entries")
     flops = C.c_int64(0)
     _check(lib().pa_measure_mfma(int(iters), _dev_ptr(out, "out"), C.byref(flops), _stream_handle(out.device)))
+    return flops.value
+
+
+def pa_measure_mfma_random(iters: int, out) -> int:
+    """bf16 matrix-core loop on N(0,1)-like operands that change with every product;
+    out as for pa_measure_mfma.  Returns the launch's flop count."""
+    if out.numel() < 65536 or out.dtype.itemsize != 4:
+        raise ValueError("out must hold 65536 32-bit entries")
+    flops = C.c_int64(0)
+    _check(lib().pa_measure_mfma_random(int(iters), _dev_ptr(out, "out"), C.byref(flops),
+                                        _stream_handle(out.device)))
     return flops.value
 
 

@@ -128,6 +128,61 @@ mfma_kernel(int32_t iters, float* __restrict__ out) {
   if ((threadIdx.x & (kWave - 1)) == 0) out[blockIdx.x * (kMeasureThreads / kWave) + threadIdx.x / kWave] = s;
 }
 
+// The same loop on operands spread like N(0,1) data: each lane holds four
+// sets of bf16 A and B operands with random sign, exponent (2^-3 .. 2^0) and
+// mantissa from an integer hash of its global index, and consecutive products
+// take different sets, so the multipliers' inputs change with every product as
+// they do on real data (the loop above feeds the same values every time).
+// iters rounds of kMfmaChains products; iters is a multiple of 4.
+__device__ __forceinline__ uint32_t mix32(uint32_t h) {  // integer finaliser (xorshift-multiply)
+  h ^= h >> 16;
+  h *= 0x7feb352du;
+  h ^= h >> 15;
+  h *= 0x846ca68bu;
+  h ^= h >> 16;
+  return h;
+}
+__device__ __forceinline__ uint32_t random_bf16_pair(uint32_t h) {
+  const uint32_t lo = (h & 0x807fu) | ((0x7cu + ((h >> 7) & 3u)) << 7);
+  const uint32_t hi = ((h >> 16) & 0x807fu) | ((0x7cu + ((h >> 23) & 3u)) << 7);
+  return lo | (hi << 16);
+}
+
+__global__ void __launch_bounds__(kMeasureThreads)
+mfma_random_kernel(int32_t iters, float* __restrict__ out) {
+  uint32_t h = mix32(threadIdx.x + blockIdx.x * kMeasureThreads + 0x9e3779b9u);
+  mbf16x8_t a[4], b[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    u32x4 av, bv;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      h = mix32(h + 1u);
+      av[k] = random_bf16_pair(h);
+      h = mix32(h + 1u);
+      bv[k] = random_bf16_pair(h);
+    }
+    a[u] = __builtin_bit_cast(mbf16x8_t, av);
+    b[u] = __builtin_bit_cast(mbf16x8_t, bv);
+  }
+  mf32x16_t acc[kMfmaChains];
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c) acc[c] = mf32x16_t{};
+  for (int32_t i = 0; i < iters; i += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < kMfmaChains; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(u + c) & 3], b[(u + 3 * c + 1) & 3], acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += acc[c][j];
+  if ((threadIdx.x & (kWave - 1)) == 0) out[blockIdx.x * (kMeasureThreads / kWave) + threadIdx.x / kWave] = s;
+}
+
 int measure_grid() {
   const int g = device_cus() * 8;
   return g < 65536 ? g : 65536;
@@ -192,4 +247,20 @@ extern "C" int pa_measure_mfma(int32_t iters, float* out, int64_t* flops, void* 
   hipLaunchKernelGGL(mfma_kernel, dim3(grid), dim3(kMeasureThreads), 0, static_cast<hipStream_t>(stream), iters, out);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : fail(PA_ERR_HIP, "pa_measure_mfma: launch failed: %s", hipGetErrorString(e));
+}
+
+extern "C" int pa_measure_mfma_random(int32_t iters, float* out, int64_t* flops, void* stream) {
+  clear_error();
+  if (!out || !flops) return fail(PA_ERR_INVALID, "pa_measure_mfma_random: null pointer");
+  if (iters <= 0 || iters % 4 != 0)
+    return fail(PA_ERR_INVALID, "pa_measure_mfma_random: iters must be a positive multiple of 4");
+  const int grid = device_cus() * kMfmaWgPerCu;
+  if (int64_t(grid) * (kMeasureThreads / kWave) > 65536)
+    return fail(PA_ERR_UNSUPPORTED, "pa_measure_mfma_random: too many compute units for the output buffer");
+  *flops = int64_t(grid) * (kMeasureThreads / kWave) * iters * kMfmaChains * (2ll * 32 * 32 * 16);
+  hipLaunchKernelGGL(mfma_random_kernel, dim3(grid), dim3(kMeasureThreads), 0, static_cast<hipStream_t>(stream), iters,
+                     out);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK
+                         : fail(PA_ERR_HIP, "pa_measure_mfma_random: launch failed: %s", hipGetErrorString(e));
 }

@@ -49,6 +49,9 @@ def test_measure_rejects_bad_arguments():
     flops = ctypes.c_int64(0)
     assert lib.pa_measure_mfma(0, 4096, ctypes.byref(flops), None) == pk.PA_ERR_INVALID
     assert lib.pa_measure_mfma(10, None, ctypes.byref(flops), None) == pk.PA_ERR_INVALID
+    assert lib.pa_measure_mfma_random(0, 4096, ctypes.byref(flops), None) == pk.PA_ERR_INVALID
+    assert lib.pa_measure_mfma_random(6, 4096, ctypes.byref(flops), None) == pk.PA_ERR_INVALID  # not a multiple of 4
+    assert lib.pa_measure_mfma_random(8, None, ctypes.byref(flops), None) == pk.PA_ERR_INVALID
 
 
 def test_reshape_rejects_bad_arguments():

@@ -68,3 +68,16 @@ def test_mfma_loop_reports_its_flops():
     assert flops == cus * 2 * 4 * iters * 4 * 2 * 32 * 32 * 16
     got = out[: cus * 2 * 4].cpu().numpy()
     assert np.isfinite(got).all() and (got != 0).all()
+
+
+def test_mfma_random_loop_reports_its_flops():
+    out = torch.zeros(65536, dtype=torch.float32, device="cuda")
+    iters = 100
+    flops = pk.pa_measure_mfma_random(iters, out)
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert flops == cus * 2 * 4 * iters * 4 * 2 * 32 * 32 * 16
+    got = out[: cus * 2 * 4].cpu().numpy()
+    assert np.isfinite(got).all() and (got != 0).all()
+    # different lanes multiply different data
+    assert len(np.unique(got)) > len(got) // 2
