@@ -104,6 +104,22 @@ def test_attention_random_steps(seed):
         _check_attention(spec, ds, out)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+def test_chunk_kernel_long_items_every_group(d, g):
+    """The MFMA chunk kernel on items of many key tiles: unmasked and masked
+    tiles, the hand-over to the next item during an item's last tiles, zeroed V
+    tails and mid-block chunk starts, for every GQA group size and head dim."""
+    seed = 200 + 10 * (d // 64) + g
+    spec = W.random_spec(seed, num_seqs=3, max_context=700, max_query=300, num_q_heads=2 * g, num_kv_heads=2,
+                         head_dim=d, dtype="bf16", decode_fraction=0.0)
+    print(f"chunk items seed={seed} d={d} g={g} (context, query)="
+          f"{[(r.context, r.query) for r in spec.requests]}", flush=True)
+    ds = build_device_step(spec)
+    ds.reshape()
+    _check_attention(spec, ds, ds.attention())
+
+
 @pytest.mark.parametrize("kernel,nbuf", [(1, 1), (1, 2), (2, 2), (2, 3), (2, 4)])
 @pytest.mark.parametrize("seed", [100, 101, 102, 103])
 def test_bf16_decode_kernels_match_oracle(seed, kernel, nbuf):
