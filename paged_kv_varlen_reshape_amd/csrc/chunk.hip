@@ -181,12 +181,31 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
   }
 
   const int n_items = w.hdr[H_TILES] * a.hkv;
+  // Items are (tile, kv head) pairs, item = tile * hkv + kv head, tiles longest
+  // first.  Tiles of one sequence and kv head re-read the same K/V prefix, so
+  // when the kv heads split evenly over the XCDs each XCD gets a queue of its
+  // own: queue x holds kv heads x, x + 8, ... of every tile, in tile order, and
+  // is served by the workgroups b with b % 8 == x, which run on XCD x and share
+  // its L2.  Every queue has gridDim.x / 8 workgroups, so every item is taken.
+  const bool xcd_queues = a.hkv % kXcdQueues == 0 && gridDim.x % kXcdQueues == 0;
+  const int xq = xcd_queues ? int(blockIdx.x % kXcdQueues) : 0;    // this workgroup's queue
+  const int q_wgs = xcd_queues ? int(gridDim.x / kXcdQueues) : int(gridDim.x);
+  const int q_len = xcd_queues ? n_items / kXcdQueues : n_items;
+  const int h_per_q = a.hkv / kXcdQueues;
+  // the j-th item of this workgroup's queue (n_items: the queue is empty)
+  auto queue_item = [&](int j) __attribute__((always_inline)) -> int {
+    if (j >= q_len) return n_items;
+    if (!xcd_queues) return j;
+    const int tl = j / h_per_q;
+    return tl * a.hkv + xq + kXcdQueues * (j - tl * h_per_q);
+  };
   const int64_t page_stride = int64_t(kBlock) * RB;
   const char* kbase = static_cast<const char*>(a.kc);
   const char* vbase = static_cast<const char*>(a.vc);
 
-  // Work queue: the workgroup's first item is blockIdx.x, later ones come from
-  // a counter (longest items first).  The next item is claimed a few key
+  // Work queue: the workgroup's first item is its queue's (blockIdx.x / 8)-th
+  // (blockIdx.x-th with a single queue), later ones come from the queue's
+  // counter (longest items first).  The next item is claimed a few key
   // tiles before the current one ends (late enough to keep the queue's
   // longest-first balance) and everything it needs before its first DMA is
   // fetched at the following tile boundaries, one dependent scalar load per
@@ -225,7 +244,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
     if (wave * kBlock < kv_end_n) mt.blk0 = cbt[int64_t(mt.seq) * a.mbps + wave];
   };
 
-  int item = blockIdx.x;
+  int item = queue_item(int(blockIdx.x) / (xcd_queues ? kXcdQueues : 1));
   Meta cur{};
   meta_stage1(item, cur);
   meta_stage2(item, cur);
@@ -240,7 +259,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
     Meta nxt{};
     auto handover = [&]() __attribute__((always_inline)) {
       if (phase == 0) {
-        if (tid == 0) claimed = int(gridDim.x) + atomicAdd(&w.hdr[H_COUNTER2], 1);
+        if (tid == 0) claimed = queue_item(q_wgs + atomicAdd(&w.hdr[H_QUEUE + xq], 1));
       } else if (phase == 1) {
         if (tid == 0) s_item = claimed;
       } else if (phase == 2) {

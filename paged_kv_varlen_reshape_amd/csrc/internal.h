@@ -20,6 +20,10 @@ constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kDecodeThreads = 256;  // 4 waves per decode workgroup
 constexpr int kPlanThreads = 1024;
 constexpr int kMaxWavesPerCU = 32;  // upper bound of resident wavefronts per CU (8 per SIMD)
+// Work queues of the chunk kernel: one per XCD of the MI355X (8 XCDs of 32 CUs,
+// each with its own L2).  Workgroups are dispatched to the XCDs round robin, so
+// workgroup b runs on XCD b % kXcdQueues.
+constexpr int kXcdQueues = 8;
 
 // ---------------------------------------------------------------- workspace
 // Plan header words at the start of the workspace: int32 words, then int64
@@ -28,7 +32,7 @@ enum PlanHeader : int {
   H_ROWS = 0,     // row-wise rows
   H_TILES = 1,    // query tiles of the MFMA chunk kernel
   H_RANGES = 2,   // decode ranges (one wavefront each, in stream order)
-  H_COUNTER2 = 9, // dynamic work counter of the chunk kernel
+  H_QUEUE = 8,    // kXcdQueues dynamic work counters of the chunk kernel (words 8..15)
   H64 = 16,       // int64 words follow
   H64_UNITS = 0,  // (row, kv head, page) units of all row-wise rows
   H64_PER = 1,    // units per decode range

@@ -17,7 +17,7 @@
 // sequences and places every tile record, row record and row's first unit
 // with one block scan; the tiles are then sorted longest first; pass 2 marks,
 // for every range, the row holding its first unit and the (row, kv head) it
-// cuts.  It also clears the work counter the chunk kernel uses.
+// cuts.  It also clears the work counters the chunk kernel uses.
 #include "internal.h"
 
 namespace pa {
@@ -238,7 +238,7 @@ plan_kernel(PlanArgs a, Workspace w) {
     w.hdr[H_ROWS] = int32_t(rows);
     w.hdr[H_TILES] = int32_t(tiles);
     w.hdr[H_RANGES] = int32_t(nranges);
-    w.hdr[H_COUNTER2] = 0;
+    for (int x = 0; x < kXcdQueues; ++x) w.hdr[H_QUEUE + x] = 0;
     w.hdr64[H64_UNITS] = units;
     w.hdr64[H64_PER] = per;
   }

@@ -120,6 +120,21 @@ def test_chunk_kernel_long_items_every_group(d, g):
     _check_attention(spec, ds, ds.attention())
 
 
+@pytest.mark.parametrize("hkv,g", [(8, 4), (16, 2)])
+def test_chunk_kernel_xcd_queues(hkv, g):
+    """Kv-head counts that split evenly over the per-XCD work queues (one or two
+    kv heads per queue) on ragged multi-tile items: every (tile, kv head) item
+    is taken exactly once."""
+    seed = 300 + hkv
+    spec = W.random_spec(seed, num_seqs=4, max_context=900, max_query=260, num_q_heads=hkv * g, num_kv_heads=hkv,
+                         head_dim=128, dtype="bf16", decode_fraction=0.0)
+    print(f"xcd queues seed={seed} hkv={hkv} g={g} (context, query)="
+          f"{[(r.context, r.query) for r in spec.requests]}", flush=True)
+    ds = build_device_step(spec)
+    ds.reshape()
+    _check_attention(spec, ds, ds.attention())
+
+
 @pytest.mark.parametrize("kernel,nbuf", [(1, 1), (1, 2), (2, 2), (2, 3), (2, 4)])
 @pytest.mark.parametrize("seed", [100, 101, 102, 103])
 def test_bf16_decode_kernels_match_oracle(seed, kernel, nbuf):
