@@ -274,7 +274,7 @@ def main(argv=None):
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(the step shards by sequence or kv head with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the step would shard by sequence or by kv head, with no exchange inside attention)", file=sys.stderr)
         return 2
 
     import torch
