@@ -43,8 +43,9 @@
 // maximum grows by more than 2^8).  Keys past a row's position get -inf by
 // select; V rows of keys past the tile's last position are zeroed in LDS after
 // the DMA (pages past the sequence are not read at all), so nothing outside
-// the sequence reaches the PV product (NaN-safe).  Tiles are taken from a
-// work counter, longest first.
+// the sequence reaches the PV product (NaN-safe).  Tiles are taken from work
+// counters, longest first: one queue per XCD when the kv heads split evenly
+// over the XCDs (the tiles of one sequence and kv head then share an L2).
 #include <type_traits>
 
 #include "internal.h"
