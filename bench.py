@@ -62,7 +62,11 @@ def algorithmic_work(spec, mfma_rows: bool, verify_rows: int = 1):
     rows = sum(r.query for r in row_reqs)
     decode_bytes = (_unique_tokens(spec, row_reqs) * kv_tok + rows * hq * d * (elt + 4)
                     + sum(-(-r.seq_len // 16) for r in row_reqs) * 4)
+    chunk_rows = sum(r.query for r in chunk_reqs)
+    chunk_bytes = (_unique_tokens(spec, chunk_reqs) * kv_tok + chunk_rows * hq * d * (elt + 4)
+                   + sum(-(-r.seq_len // 16) for r in chunk_reqs) * 4)
     return dict(kv_unique_bytes=_unique_tokens(spec, spec.requests) * kv_tok,
+                chunk_kernel_bytes=chunk_bytes,
                 kv_logical_bytes=sum(r.seq_len for r in spec.requests) * kv_tok,
                 decode_kernel_bytes=decode_bytes,
                 causal_flops=sum(pair_flops(r) for r in spec.requests),
@@ -352,8 +356,10 @@ def main(argv=None):
     use_mfma = spec.dtype == "bf16" and pk.pa_get_option(pk.PA_OPT_FORCE_ROWWISE) == 0 and prof["chunk_mfma"][0] > 0
     g = spec.num_q_heads // spec.num_kv_heads
     vr_opt = pk.pa_get_option(pk.PA_OPT_VERIFY_ROWS)
+    # short queries go row-wise only when the option asks for it (the library's
+    # default sends them to the chunk kernel), capped at one 16-wide accumulator
     verify = (1 if spec.dtype != "bf16" or pk.pa_get_option(pk.PA_OPT_DECODE_KERNEL) == 1
-              or pk.pa_get_option(pk.PA_OPT_FORCE_ROWWISE) else min(vr_opt or 16 // g, 16 // g))
+              or pk.pa_get_option(pk.PA_OPT_FORCE_ROWWISE) or vr_opt < 1 else min(vr_opt, 16 // g))
     work = algorithmic_work(spec, use_mfma, verify)
     ms = dt * 1e3 / args.steps
     decode_n, decode_ms = prof["decode"]
@@ -371,7 +377,20 @@ def main(argv=None):
     else:
         value = work["kv_unique_bytes"] / (ms * 1e-3) / 1e9
         unit = "GB/s"
-    if use_mfma and prefill_like:
+    # a step whose rows all go to the chunk kernel is judged by that kernel: on the
+    # matrix cores above the ridge point (flops per HBM byte), else on HBM
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    chunk_only = use_mfma and chunk_n > 0 and decode_n == 0
+    chunk_hbm = chunk_only and not prefill_like and work["chunk_flops"] < ridge * work["chunk_kernel_bytes"]
+    if chunk_hbm:
+        ach = work["chunk_kernel_bytes"] / (chunk_avg * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS,
+                    traffic=recorded_traffic("chunk_mfma", spec.cfg_id), kernel="chunk_mfma",
+                    kernel_avg_us=chunk_avg * 1e3, algorithmic_bytes=work["chunk_kernel_bytes"])
+        if ceil:
+            roof["frac_of_measured_read"] = ach / ceil["read_GBps"]
+            roof["frac_of_measured_gather4k"] = ach / ceil["gather4k_GBps"]
+    elif use_mfma and (prefill_like or chunk_only):
         ach = work["chunk_flops"] / (chunk_avg * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=ach, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=ach / MFMA_BF16_PEAK_TFLOPS, traffic=recorded_traffic("chunk_mfma", spec.cfg_id),
