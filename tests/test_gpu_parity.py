@@ -135,6 +135,20 @@ def test_chunk_kernel_xcd_queues(hkv, g):
     _check_attention(spec, ds, ds.attention())
 
 
+def test_chunk_and_decode_over_very_long_contexts():
+    """A 200-row chunk over 40000 cached tokens (about 630 key tiles per item,
+    with the next item claimed during its last tiles), a decode over 100000
+    tokens cut into many ranges, and a short 5-row chunk, GQA 8:1 with one kv head."""
+    reqs = [W.Request(0, 40000, 200), W.Request(1, 100000, 1), W.Request(2, 37, 5)]
+    nb = sum(-(-r.seq_len // 16) for r in reqs) + 4
+    order = np.random.default_rng((77, 0)).permutation(nb).astype(np.int32)
+    spec = W.StepSpec("long-contexts", 77, 8, 1, 128, "bf16", 16, nb, 1.0 / np.sqrt(128.0), reqs,
+                      initial_order=order, seed=77)
+    ds = build_device_step(spec)
+    ds.reshape()
+    _check_attention(spec, ds, ds.attention())
+
+
 @pytest.mark.parametrize("kernel,nbuf", [(1, 1), (1, 2), (2, 2), (2, 3), (2, 4)])
 @pytest.mark.parametrize("seed", [100, 101, 102, 103])
 def test_bf16_decode_kernels_match_oracle(seed, kernel, nbuf):
