@@ -168,14 +168,37 @@ def pa_attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, c
     max_query_len: the step's longest query as the caller knows it (host int); None passes T (unknown)."""
     import torch
 
+    # the library sees only pointers and sizes: every size it derives from
+    # these tensors is checked here, before any kernel could read past one
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [T, Hq, D] and k_cache [NB, Hkv, 16, D]")
     T, hq, d = q.shape
     nb, hkv, bs, d2 = k_cache.shape
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("v_cache must have k_cache's shape")
+    if d2 != d:
+        raise ValueError(f"q has head_dim {d}, the caches {d2}")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share one dtype")
     S = seq_lens.numel()
-    mbps = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    if block_tables.dim() != 2 or (S > 0 and block_tables.shape[0] != S):
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    mbps = block_tables.shape[1]
+    if context_lens.numel() != S or query_start_loc.numel() != S + 1:
+        raise ValueError("seq_lens and context_lens need num_seqs entries, query_start_loc num_seqs + 1")
     for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"), (query_start_loc, "query_start_loc"),
                  (context_lens, "context_lens")):
         if t.dtype != torch.int32:
             raise ValueError(f"{n} must be int32")
+    devices = {t.device for t in (q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens)}
+    if out is not None:
+        if tuple(out.shape) != (T, hq, d) or out.dtype != torch.float32:
+            raise ValueError("out must be float32 [T, Hq, D]")
+        devices.add(out.device)
+    if workspace is not None:
+        devices.add(workspace.device)
+    if len(devices) != 1:
+        raise ValueError("all tensors must be on one device")
     if out is None:
         out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
     need = pa_attention_workspace_size(S, T, hq, hkv, d, mbps)
