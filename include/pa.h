@@ -143,7 +143,7 @@ const char* pa_last_error(void);
 
 /* Tuning and debug options (process-wide).  Returns PA_OK or PA_ERR_INVALID. */
 enum {
-  PA_OPT_FORCE_ROWWISE = 1,  /* 1: every query row takes the row-wise VALU kernel, MFMA off */
+  PA_OPT_FORCE_ROWWISE = 1,  /* 1: every query row takes a row-wise kernel (the chunk kernel is off) */
   PA_OPT_SPLIT_TOKENS = 2,   /* >0: each decode wavefront range covers this many tokens' worth of
                                 (row, kv head) pages (multiple of 16); 0: automatic, the step's
                                 pages spread evenly over the resident wavefronts */

@@ -28,8 +28,11 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
-# per-file device flags: the chunk kernel never lets a NaN reach its math
-# (masked keys are not loaded), so max/min need no NaN canonicalisation
+# per-file device flags: in the chunk kernel no NaN reaches a maximum or the
+# softmax (keys past a row's position are replaced by -inf before the maximum,
+# V rows past the sequence are zeroed, and the factor the raw scores are
+# multiplied by is positive, the host having folded a negative or zero scale
+# into Q), so max/min need no NaN canonicalisation
 FILE_FLAGS = {"chunk.hip": ["-fno-honor-nans"]}
 
 SOURCES = ["errors.cpp", "pool.cpp", "validate.cpp", "api.hip", "reshape.hip", "plan.hip",

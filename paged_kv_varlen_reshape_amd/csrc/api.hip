@@ -1,6 +1,7 @@
 // C-ABI entry points of libpa: argument checks, workspace layout and the
 // launch sequence of one step (scatter; plan -> chunk -> row-wise split-K -> split merge).
 #include <atomic>
+#include <cfloat>
 #include <cmath>
 #include <mutex>
 #include <vector>
@@ -244,6 +245,18 @@ extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_ca
   a.ctx = context_lens;
   a.out = out;
   a.scale_log2 = scale * 1.4426950408889634f;
+  {
+    const float mag = std::fabs(scale) * 1.4426950408889634f;
+    if (mag < FLT_MIN) {  // zero (or below the normal range: every weight equal to fp32 precision)
+      a.chunk_scale_log2 = 1.f;
+      a.q_and = 0u;
+      a.q_xor = 0u;
+    } else {
+      a.chunk_scale_log2 = mag;
+      a.q_and = ~0u;
+      a.q_xor = scale < 0.f ? 0x80008000u : 0u;
+    }
+  }
   a.num_seqs = num_seqs;
   a.num_tokens = num_tokens;
   a.hq = num_q_heads;

@@ -38,7 +38,11 @@
 //
 // Online softmax in the log2 domain on the VALU; P is rounded to bf16 for the
 // PV product and the row sum l adds the rounded values, so the output is an
-// exact convex combination of V rows with the rounded weights.  The reference
+// exact convex combination of V rows with the rounded weights.  Row maxima are
+// taken on raw scores and then multiplied by the scale, which is therefore
+// kept positive: the host folds a negative scale's sign into Q (a bf16 sign
+// flip, exact) and turns a zero scale into a zeroed Q, so masked keys (-inf)
+// always end as weight 0 and never meet a factor of 0.  The reference
 // maximum moves lazily (the O accumulators are rescaled only when a row's
 // maximum grows by more than 2^8).  Keys past a row's position get -inf by
 // select; V rows of keys past the tile's last position are zeroed in LDS after
@@ -295,6 +299,12 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
                                                        ((int64_t(r0) + t0 + tt) * a.hq + head) * RB);
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = valid ? qp[2 * kk + lg] : u32x4{0u, 0u, 0u, 0u};
+      // a negative or zero scale: its sign (or the zero) goes into Q, so the
+      // factor the scores are multiplied by below is always positive
+      if (a.q_and != ~0u || a.q_xor != 0u) {
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = (qf[kk] & a.q_and) ^ a.q_xor;
+      }
     }
 
     f32x16_t o[DBLK];
@@ -434,7 +444,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
       float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
       for (int j = 1; j < 16; ++j) mx = fmaxf(fmaxf(mx, s[0][j]), s[1][j]);
-      mx = pair_max(mx) * a.scale_log2;
+      mx = pair_max(mx) * a.chunk_scale_log2;
       // wave-uniform branch (rarely taken after the first tiles); lanes whose
       // maximum did not grow scale by 1
       const bool grow = mx > m + 8.f;
@@ -454,8 +464,8 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float p0 = fast_exp2(fmaf(s[mb][2 * i], a.scale_log2, -m_use));
-          const float p1 = fast_exp2(fmaf(s[mb][2 * i + 1], a.scale_log2, -m_use));
+          const float p0 = fast_exp2(fmaf(s[mb][2 * i], a.chunk_scale_log2, -m_use));
+          const float p1 = fast_exp2(fmaf(s[mb][2 * i + 1], a.chunk_scale_log2, -m_use));
           pk[mb][i] = pack_bf16(p0, p1);
           l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[mb][i]), kOnes, l, false);
         }

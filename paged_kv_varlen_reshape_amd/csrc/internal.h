@@ -132,6 +132,14 @@ struct AttnArgs {
   const int32_t* ctx;
   float* out;
   float scale_log2;  // scale * log2(e)
+  // The chunk kernel takes row maxima of raw scores and multiplies them by a
+  // positive factor, chunk_scale_log2 = |scale| * log2(e) (1 for a zero scale);
+  // the rest of the scale goes into its Q operand, each dword ANDed with q_and
+  // and XORed with q_xor: a negative scale flips every bf16 sign bit (exact:
+  // every score changes sign and nothing else), a zero scale zeroes Q (every
+  // score exactly 0, as scale * <q, K> is).  Identity: q_and = ~0, q_xor = 0.
+  float chunk_scale_log2;
+  uint32_t q_and, q_xor;
   int32_t num_seqs, num_tokens, hq, hkv, d, mbps;
   int64_t nb;
   int32_t bf16;

@@ -4,7 +4,8 @@ The library allocates nothing, clears its counters with kernels (no memset
 nodes) and never synchronises, so a step can be captured once per batch shape
 and replayed.  Each replay must reproduce the eager step bit for bit (the
 kernels are deterministic), with eager work and synchronisations between the
-replays.  The eager step itself is checked against the oracle elsewhere.
+replays, and the replayed output is checked against the fp64 oracle on every
+row (max-abs 1e-5 for float32 steps, 1e-2 for bf16).
 """
 import numpy as np
 import pytest
@@ -13,8 +14,10 @@ import torch
 import paged_kv_varlen_reshape_amd as pk
 import workloads as W
 from workloads.device import build_device_step
+from device_data import oracle_rows
 
 pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-5, "bf16": 1e-2}
 
 
 def _specs():
@@ -61,3 +64,7 @@ def test_step_replays_from_a_graph(name, spec):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {rep} differs from the eager step"
+    want, got = oracle_rows(spec, range(spec.num_seqs), out, ds.meta)
+    err = float(np.abs(want - got).max())
+    print(f"graph replay {name}: max_abs_err vs oracle {err:.3e}", flush=True)
+    assert err <= TOL[spec.dtype], err
