@@ -30,6 +30,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "decode KV-read GB/s (% HBM peak); prefill/mixed TFLOP/s (% MFMA peak)"
+
+
+def log(msg: str) -> None:
+    """Progress of the run on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
@@ -199,6 +204,7 @@ def cpu_baseline(spec, seconds: float):
             n_seq += 1
             if busy >= seconds:
                 break
+        log(f"oracle: {n_seq} sequence passes, {busy:.1f} s timed")
     return dict(bytes_per_s=done_bytes / busy, flops_per_s=done_flops / busy, cores=cores,
                 sample=f"{n_seq} sequence passes of the oracle (numpy float64 causal attention, K/V regenerated "
                        f"from the seeded tables untimed) over {len(order)} sequences of this workload, "
@@ -311,11 +317,15 @@ def main(argv=None):
     if args.engine:
         return engine_bench(args, pk, torch)
     ceil = None if args.no_ceilings else measure_ceilings(pk, torch)
+    if ceil:
+        log("ceilings: " + ", ".join(f"{k}={v:.0f}" for k, v in ceil.items()))
     spec = W.make_config(args.config)
     # rotate over enough replicas that the K/V read since a replica's last use
     # exceeds 1 GiB (4x the 256 MB last-level cache)
     kv_step = algorithmic_work(spec, False)["kv_unique_bytes"]
     reps = args.replicas or (1 if kv_step >= (1 << 30) else min(8, -(-(1 << 30) // max(1, kv_step)) + 1))
+    log(f"building {reps} replica(s) of configuration {spec.cfg_id}: {spec.num_seqs} sequences, "
+        f"{spec.num_tokens} query tokens, {spec.num_blocks} blocks")
     steps = [build_device_step(spec, device="cuda:0") for _ in range(reps)]
     outs = [torch.empty((spec.num_tokens, spec.num_q_heads, spec.head_dim), dtype=torch.float32, device="cuda:0")
             for _ in range(reps)]
@@ -346,11 +356,13 @@ def main(argv=None):
         for i in range(args.warmup):
             run(i)
         torch.cuda.synchronize()
+    log("inputs resident; timed pass")
     t0 = time.perf_counter()
     for i in range(args.steps):
         run(args.warmup + i)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    log(f"timed pass: {dt * 1e3 / args.steps:.3f} ms per step; per-kernel event pass")
     # second pass with HIP-event timing around every kernel launch of the step
     # (kept out of the step timing above: the extra event records cost time)
     pk.pa_profile_enable((1 << pk.PA_K_COUNT) - 1)
@@ -446,6 +458,7 @@ def main(argv=None):
         "ceilings": ceil,
     }
     if not args.no_cpu_baseline:
+        log("oracle CPU baseline")
         cb = cpu_baseline(spec, args.cpu_seconds)
         res["cpu_baseline"] = {"value": cb["flops_per_s"] / 1e12 if prefill_like else cb["bytes_per_s"] / 1e9,
                                "unit": unit, "cores": cb["cores"], "kind": "oracle", "sample": cb["sample"]}

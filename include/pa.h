@@ -61,6 +61,13 @@ typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
 
 /* Scatter the step's new K and V rows into the paged caches.
  *
+ * The K/V of every token a request holds lives in the 16-token blocks it was
+ * given, block by block in token order (Inside vLLM summary, techfeed.io,
+ * section "PagedAttentionの仕組み": block size 16, blocks taken per request
+ * into req_to_blocks); the step's new tokens are written into their slots
+ * before attention reads them.  Slot s = block id * 16 + position % 16 is
+ * this library's reading of that layout.
+ *
  * For every token n < num_tokens with s = slot_mapping[n] >= 0 and every kv
  * head h:  k_cache[s/16][h][s%16][:] = k[n][h][:]  (and the same for v).
  * The copy is of raw element bits.  A negative slot skips the token.
@@ -80,7 +87,13 @@ int pa_reshape_and_cache(const void* k, const void* v, const int32_t* slot_mappi
                          int64_t num_blocks, int32_t dtype, void* stream);
 
 /* Bytes of device workspace pa_attention needs for a step of this shape
- * (work lists, partial results of split rows, counters).  Depends on the
+ * (work lists, partial results of split rows, counters).  Decoding reads the
+ * whole cached context of every request and is bound by memory bandwidth
+ * (Inside vLLM summary, section "エンジンの中核：スケジューラとKVキャッシュ管理"),
+ * so pa_attention spreads each step's pages evenly over the whole GPU and
+ * merges the pieces of rows it splits; the workspace holds those pieces.
+ * The pool size does not enter (the pages are reached through block_tables);
+ * the group size num_q_heads / num_kv_heads does.  Depends on the
  * arguments, the current device's compute-unit count and the options, so it
  * can be sized once for the largest step and reused.  Returns 0 if the
  * arguments are invalid. */
@@ -90,11 +103,22 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t
 
 /* Attention of every query row of the step over its own sequence's paged K/V.
  *
+ * All requests of a step are flattened into one super-sequence whose
+ * positions and attention mask keep each request attending to its own tokens
+ * only (Inside vLLM summary, techfeed.io, section "PagedAttentionの仕組み"),
+ * and one step mixes prefill chunks with single-token decodes (section
+ * "エンジンの中核：スケジューラとKVキャッシュ管理"; chunked prefill in section
+ * "高度な機能群").  Causal alignment (a row at position p sees keys 0..p),
+ * the GQA mapping and the scale's place before the maximum are this library's
+ * readings where the pages are silent.
+ *
  * Sequence i owns query rows [query_start_loc[i], query_start_loc[i+1]); its
  * row j sits at absolute position p = context_lens[i] + j and sees the keys at
  * positions 0..p (itself included), read through block_tables[i].  Query head
  * h reads kv head h / (num_q_heads / num_kv_heads).  For each row and head:
  *   out = sum_t softmax_t(scale * <q, K_t>) V_t,  t = 0..p      (float32)
+ * for any finite scale (0 weighs every visible key equally; a non-finite
+ * scale is PA_ERR_INVALID).
  *
  *   q                [num_tokens, num_q_heads, head_dim], dtype
  *   k_cache, v_cache [num_blocks, num_kv_heads, 16, head_dim], dtype
