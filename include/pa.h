@@ -151,6 +151,26 @@ int pa_attention(const void* q, const void* k_cache, const void* v_cache,
                  int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
                  int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_attention for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, checks, kernels and results as pa_attention, without the
+ * workspace: the library keeps one static device array of
+ * PA_NOALLOC_WORKSPACE_MAX bytes per GPU it runs on (held until the process
+ * ends) and uses it in place of the caller's buffer.  Calls nothing that
+ * allocates.  A step whose pa_attention_workspace_size exceeds
+ * PA_NOALLOC_WORKSPACE_MAX is rejected with PA_ERR_WORKSPACE before any launch.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (two streams or two threads at once) race and must be serialised by the
+ * caller; calls on the same stream are ordered and safe. */
+#define PA_NOALLOC_WORKSPACE_MAX (96u << 20)
+int pa_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens,
+                         const int32_t* query_start_loc, const int32_t* context_lens, float scale,
+                         float* out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                         int32_t dtype, void* stream);
+
 /* Check step metadata on host copies, O(num_tokens + num_seqs*max_blocks).
  *   seq_lens[i] == context_lens[i] + (query_start_loc[i+1]-query_start_loc[i]) >= 0,
  *   query_start_loc[0] == 0, non-decreasing, query_start_loc[num_seqs] == num_tokens,

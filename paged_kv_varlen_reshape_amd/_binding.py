@@ -43,6 +43,8 @@ SIGNATURES = {
     "pa_attention_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_attention": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32,
                             _i32, _i64, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_attention_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                    _i32, _i64, _i32, _i32, _i32, _vp]),
     "pa_validate_metadata": (_i32, [_pi32, _pi32, _pi32, _pi32, _pi32, _i32, _i32, _i32, _i64, _i32]),
     "pa_last_error": (C.c_char_p, []),
     "pa_set_option": (_i32, [_i32, _i64]),
@@ -211,6 +213,41 @@ def pa_attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, c
                               T if max_query_len is None else int(max_query_len), _dtype_code(q),
                               _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                               _stream_handle(q.device)))
+    return out
+
+
+def pa_attention_noalloc(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens, scale: float,
+                         out, max_query_len=None):
+    """pa_attention with the library's static per-GPU workspace instead of a caller buffer
+    (nothing is allocated: `out` must be given).  Calls that overlap on one GPU race."""
+    import torch
+
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [T, Hq, D] and k_cache [NB, Hkv, 16, D]")
+    T, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or d2 != d or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches disagree in shape or dtype")
+    S = seq_lens.numel()
+    if block_tables.dim() != 2 or (S > 0 and block_tables.shape[0] != S):
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if context_lens.numel() != S or query_start_loc.numel() != S + 1:
+        raise ValueError("seq_lens and context_lens need num_seqs entries, query_start_loc num_seqs + 1")
+    for t in (block_tables, seq_lens, query_start_loc, context_lens):
+        if t.dtype != torch.int32:
+            raise ValueError("index arrays must be int32")
+    if tuple(out.shape) != (T, hq, d) or out.dtype != torch.float32:
+        raise ValueError("out must be float32 [T, Hq, D]")
+    if len({t.device for t in (q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens,
+                               out)}) != 1:
+        raise ValueError("all tensors must be on one device")
+    _check(lib().pa_attention_noalloc(_dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                                      _dev_ptr(block_tables, "block_tables"), _dev_ptr(seq_lens, "seq_lens"),
+                                      _dev_ptr(query_start_loc, "query_start_loc"),
+                                      _dev_ptr(context_lens, "context_lens"), float(scale), _dev_ptr(out, "out"),
+                                      S, T, hq, hkv, d, bs, nb, block_tables.shape[1],
+                                      T if max_query_len is None else int(max_query_len), _dtype_code(q),
+                                      _stream_handle(q.device)))
     return out
 
 

@@ -36,7 +36,7 @@ COMMON = ["-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", INCLUDE,
 FILE_FLAGS = {"chunk.hip": ["-fno-honor-nans"]}
 
 SOURCES = ["errors.cpp", "pool.cpp", "validate.cpp", "api.hip", "reshape.hip", "plan.hip",
-           "decode.hip", "decode_mfma.hip", "chunk.hip", "measure.hip"]
+           "decode.hip", "decode_mfma.hip", "chunk.hip", "measure.hip", "noalloc.hip"]
 
 
 def _compile(src: str, opt: list[str]) -> str:

@@ -169,37 +169,40 @@ extern "C" size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_toke
   return layout_workspace(s, nullptr).bytes;
 }
 
-extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                            const int32_t* seq_lens, const int32_t* query_start_loc, const int32_t* context_lens,
-                            float scale, float* out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
-                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                            int32_t max_blocks_per_seq, int32_t max_query_len, int32_t dtype, void* workspace,
-                            size_t workspace_bytes, void* stream) {
-  clear_error();
-  if (int rc = check_dims(num_kv_heads, head_dim, block_size, dtype, num_blocks, "pa_attention")) return rc;
+namespace pa {
+
+int check_attention_args(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                         const int32_t* seq_lens, const int32_t* query_start_loc, const int32_t* context_lens,
+                         float scale, float* out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                         int32_t max_blocks_per_seq, int32_t dtype, const char* who) {
+  if (int rc = check_dims(num_kv_heads, head_dim, block_size, dtype, num_blocks, who)) return rc;
   if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
-    return fail(PA_ERR_INVALID, "pa_attention: num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+    return fail(PA_ERR_INVALID, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", who, num_q_heads,
                 num_kv_heads);
   const int group = num_q_heads / num_kv_heads;
   if (group != 1 && group != 2 && group != 4 && group != 8)
-    return fail(PA_ERR_UNSUPPORTED, "pa_attention: query heads per kv head = %d (1, 2, 4 or 8 are built)", group);
-  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq < 0)
-    return fail(PA_ERR_INVALID, "pa_attention: negative size");
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "pa_attention: scale is not finite");
+    return fail(PA_ERR_UNSUPPORTED, "%s: query heads per kv head = %d (1, 2, 4 or 8 are built)", who, group);
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq < 0) return fail(PA_ERR_INVALID, "%s: negative size", who);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "%s: scale is not finite", who);
   if (num_tokens == 0 || num_seqs == 0) return PA_OK;
-  if (max_blocks_per_seq == 0) return fail(PA_ERR_INVALID, "pa_attention: max_blocks_per_seq is 0 with query rows");
+  if (max_blocks_per_seq == 0) return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq is 0 with query rows", who);
   if (int64_t(max_blocks_per_seq) * kBlock >= (int64_t(1) << 31))
-    return fail(PA_ERR_INVALID, "pa_attention: max_blocks_per_seq too large");
+    return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq too large", who);
   if (int64_t(num_kv_heads) * max_blocks_per_seq >= (int64_t(1) << 31))  // one row's pages over all kv heads
-    return fail(PA_ERR_INVALID, "pa_attention: num_kv_heads * max_blocks_per_seq too large");
+    return fail(PA_ERR_INVALID, "%s: num_kv_heads * max_blocks_per_seq too large", who);
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !context_lens || !out)
-    return fail(PA_ERR_INVALID, "pa_attention: null pointer");
+    return fail(PA_ERR_INVALID, "%s: null pointer", who);
+  return PA_OK;
+}
+
+int run_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                  const int32_t* seq_lens, const int32_t* query_start_loc, const int32_t* context_lens, float scale,
+                  float* out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                  int32_t dtype, void* workspace, void* stream, const char* who) {
+  const int group = num_q_heads / num_kv_heads;
   StepShape shape{num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq};
-  const size_t need = layout_workspace(shape, nullptr).bytes;
-  if (!workspace || workspace_bytes < need)
-    return fail(PA_ERR_WORKSPACE, "pa_attention: workspace of %zu bytes, %zu needed", workspace_bytes, need);
-  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(PA_ERR_WORKSPACE, "pa_attention: workspace must be 256-byte aligned");
 
   const Workspace w = layout_workspace(shape, workspace);
   const bool bf16 = dtype == PA_BF16;
@@ -292,8 +295,34 @@ extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_ca
     // automatic ranges number at most num_ranges; fixed-length ones up to the capacity
     e = launch_merge(a, w, group, pa_args.fixed_units > 0 ? w.ranges_cap : pa_args.num_ranges, st);
   }
-  if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_attention: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return PA_OK;
+}
+
+}  // namespace pa
+
+extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            const int32_t* seq_lens, const int32_t* query_start_loc, const int32_t* context_lens,
+                            float scale, float* out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                            int32_t max_blocks_per_seq, int32_t max_query_len, int32_t dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  clear_error();
+  static const char* who = "pa_attention";
+  if (int rc = check_attention_args(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens, scale,
+                                    out, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
+                                    num_blocks, max_blocks_per_seq, dtype, who))
+    return rc;
+  if (num_tokens == 0 || num_seqs == 0) return PA_OK;
+  StepShape shape{num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq};
+  const size_t need = layout_workspace(shape, nullptr).bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "pa_attention: workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(PA_ERR_WORKSPACE, "pa_attention: workspace must be 256-byte aligned");
+  return run_attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens, scale, out,
+                       num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq,
+                       max_query_len, dtype, workspace, stream, who);
 }
 
 extern "C" int pa_profile_enable(int32_t mask) {

@@ -165,6 +165,20 @@ int chunk_tile_rows(int group);
 
 int device_cus();
 
+// pa_attention's argument checks (PA_OK, or the error it reports for `who`) and
+// its launch sequence on an already checked call with a workspace of at least
+// layout_workspace(...).bytes at a 256-byte-aligned device address.
+int check_attention_args(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                         const int32_t* seq_lens, const int32_t* query_start_loc, const int32_t* context_lens,
+                         float scale, float* out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                         int32_t max_blocks_per_seq, int32_t dtype, const char* who);
+int run_attention(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                  const int32_t* seq_lens, const int32_t* query_start_loc, const int32_t* context_lens, float scale,
+                  float* out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                  int32_t dtype, void* workspace, void* stream, const char* who);
+
 // Scoped HIP-event timing of one launch (active only when its kind is enabled).
 class KernelTimer {
  public:

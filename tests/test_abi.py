@@ -128,3 +128,24 @@ def test_options_roundtrip_and_errors():
         pk.pa_set_option(pk.PA_OPT_VERIFY_ROWS, 17)
     with pytest.raises(pk.PAError):
         pk.pa_set_option(99, 0)
+
+
+def test_noalloc_attention_rejects_bad_arguments_and_oversized_steps():
+    """pa_attention_noalloc: pa_attention's argument checks, and a step whose workspace
+    exceeds the static per-GPU array is refused before anything is launched."""
+    lib = pk.lib()
+
+    def call(hq=8, hkv=2, d=128, bs=16, nb=64, mbps=4, S=2, T=3, dtype=pk.PA_BF16, ptr=1, scale=0.1):
+        p = ptr
+        return lib.pa_attention_noalloc(p, p, p, p, p, p, p, scale, p, S, T, hq, hkv, d, bs, nb, mbps, T, dtype,
+                                        None)
+
+    assert call(hq=6, hkv=4) == pk.PA_ERR_INVALID
+    assert call(d=80) == pk.PA_ERR_UNSUPPORTED
+    assert call(ptr=None) == pk.PA_ERR_INVALID
+    assert call(scale=float("inf")) == pk.PA_ERR_INVALID
+    assert call(T=0, ptr=None) == pk.PA_OK
+    big_T = 4 << 20
+    assert pk.pa_attention_workspace_size(1, big_T, 8, 1, 128, 8) > (96 << 20)
+    assert call(hq=8, hkv=1, S=1, T=big_T, mbps=8) == pk.PA_ERR_WORKSPACE
+    assert "static scratch" in pk.last_error()
