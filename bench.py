@@ -295,6 +295,8 @@ def main(argv=None):
     ap.add_argument("--engine-blocks", type=int, default=2560, help="pool size of the engine run")
     ap.add_argument("--graph", action="store_true",
                     help="replay each replica's step from a captured HIP graph (one capture per replica)")
+    ap.add_argument("--graph-steps", type=int, default=1,
+                    help="steps (of consecutive replicas) captured in one graph, replayed with one launch")
     ap.add_argument("--opt", action="append", default=[], metavar="NAME=VALUE",
                     help="library option before the run, e.g. DECODE_BUFFERS=1")
     args = ap.parse_args(argv)
@@ -340,29 +342,37 @@ def main(argv=None):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    run = step
+    # a launch runs `per_launch` consecutive steps: one eager step, or one replay of a
+    # graph that holds --graph-steps steps (of consecutive replicas)
+    per_launch = 1
+    launch = step
     if args.graph:
+        per_launch = max(1, args.graph_steps)
         graphs = []
         for r in range(reps):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(r)
+                for k in range(per_launch):
+                    step(r + k)
             graphs.append(g)
         torch.cuda.synchronize()
 
-        def run(i):
-            graphs[i % reps].replay()
+        def launch(j):
+            graphs[j % reps].replay()
 
-        for i in range(args.warmup):
-            run(i)
+        for j in range(args.warmup):
+            launch(j)
         torch.cuda.synchronize()
+    launches = -(-args.steps // per_launch)
+    n_steps = launches * per_launch
     log("inputs resident; timed pass")
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        run(args.warmup + i)
+    for j in range(launches):
+        launch(args.warmup + j)
+    t_issue = time.perf_counter() - t0  # host time to issue every launch (the GPU may still run)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    log(f"timed pass: {dt * 1e3 / args.steps:.3f} ms per step; per-kernel event pass")
+    log(f"timed pass: {dt * 1e3 / n_steps:.3f} ms per step; per-kernel event pass")
     # second pass with HIP-event timing around every kernel launch of the step
     # (kept out of the step timing above: the extra event records cost time)
     pk.pa_profile_enable((1 << pk.PA_K_COUNT) - 1)
@@ -373,13 +383,13 @@ def main(argv=None):
     prof = pk.pa_profile_read()
     pk.pa_profile_enable(0)
     # third pass: HIP events around each whole step, for its spread (p10 / median / p90)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.steps):
-        evs[i][0].record()
-        run(args.warmup + i)
-        evs[i][1].record()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for j in range(launches):
+        evs[j][0].record()
+        launch(args.warmup + j)
+        evs[j][1].record()
     torch.cuda.synchronize()
-    step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    step_us = sorted(a.elapsed_time(b) * 1e3 / per_launch for a, b in evs)
     pct = lambda q: step_us[min(len(step_us) - 1, int(q * (len(step_us) - 1) + 0.5))]
 
     use_mfma = spec.dtype == "bf16" and pk.pa_get_option(pk.PA_OPT_FORCE_ROWWISE) == 0 and prof["chunk_mfma"][0] > 0
@@ -390,7 +400,7 @@ def main(argv=None):
     verify = (1 if spec.dtype != "bf16" or pk.pa_get_option(pk.PA_OPT_DECODE_KERNEL) == 1
               or pk.pa_get_option(pk.PA_OPT_FORCE_ROWWISE) or vr_opt < 1 else min(vr_opt, 16 // g))
     work = algorithmic_work(spec, use_mfma, verify)
-    ms = dt * 1e3 / args.steps
+    ms = dt * 1e3 / n_steps
     decode_n, decode_ms = prof["decode"]
     # the row-wise kernel bf16 steps take unless an option picks the VALU one
     decode_kernel = ("decode_mfma" if spec.dtype == "bf16" and pk.pa_get_option(pk.PA_OPT_DECODE_KERNEL) != 1
@@ -445,7 +455,7 @@ def main(argv=None):
                                       kernel_avg_us=chunk_avg * 1e3, algorithmic_flops=work["chunk_flops"],
                                       traffic=recorded_traffic("chunk_mfma", spec.cfg_id))
     res = {
-        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": n_steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": spec.dtype, "data": "synthetic",
         "config": {"workload": workload_desc(spec), "num_seqs": spec.num_seqs, "num_tokens": spec.num_tokens,
@@ -454,7 +464,9 @@ def main(argv=None):
         "roofline": roof,
         "kernels_avg_us": {k: (v[1] / v[0] * 1e3 if v[0] else None) for k, v in prof.items()},
         "step_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
-        "launch": "hip_graph" if args.graph else "stream",
+        "launch": (f"hip_graph ({per_launch} step{'s' if per_launch > 1 else ''} per replay)" if args.graph
+                   else "stream"),
+        "host_issue_us_per_step": t_issue * 1e6 / n_steps,
         "ceilings": ceil,
     }
     if not args.no_cpu_baseline:

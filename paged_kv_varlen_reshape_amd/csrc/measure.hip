@@ -1,9 +1,14 @@
 // Ceiling kernels: streaming copy, read-only reduction and random page gather
 // over HBM, and a bf16 matrix-core loop.
 //
-// A grid of a few workgroups per CU walks the buffer with 16-byte lanes, each
-// thread keeping four independent loads in flight per iteration, so the
-// kernels are bound by HBM and not by issue.
+// Streaming read and copy: each wavefront takes contiguous runs of the buffer
+// (16 KiB for the read, 8 KiB for the copy: 16 or 8 16-byte loads per lane, all
+// in flight together) and the runs go round robin over the wavefronts of a
+// grid of 16 (read) or 4 (copy) workgroups per CU.  Nontemporal loads and
+// stores.  On the MI355X these layouts measured fastest among runs of 1..16
+// KiB and grids of 4..16 workgroups per CU (read about 7.0 TB/s, copy about
+// 5.4 TB/s counting read and write bytes), so the ceilings are not set by
+// issue or latency.
 #include "internal.h"
 #include "pa_measure.h"
 
@@ -11,47 +16,60 @@ namespace pa {
 namespace {
 
 constexpr int kMeasureThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kReadRun = 16;  // 1 KiB pieces per wavefront run of the read
+constexpr int kCopyRun = 8;   // 1 KiB pieces per wavefront run of the copy
+constexpr int kReadWgPerCu = 16;
+constexpr int kCopyWgPerCu = 4;
 
 __global__ void __launch_bounds__(kMeasureThreads)
 copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src, int64_t n) {
-  const int64_t stride = int64_t(gridDim.x) * kMeasureThreads;
-  int64_t i = int64_t(blockIdx.x) * kMeasureThreads + threadIdx.x;
-  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
-    u32x4 v[kUnroll];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t waves = int64_t(gridDim.x) * (kMeasureThreads / kWave);
+  const int64_t wave = int64_t(blockIdx.x) * (kMeasureThreads / kWave) + threadIdx.x / kWave;
+  const int64_t runs = n / (int64_t(kCopyRun) * kWave);
+  for (int64_t r = wave; r < runs; r += waves) {
+    const int64_t o = r * kCopyRun * kWave + lane;
+    u32x4 v[kCopyRun];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int c = 0; c < kCopyRun; ++c) v[c] = __builtin_nontemporal_load(src + o + c * kWave);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) __builtin_nontemporal_store(v[u], dst + i + u * stride);
+    for (int c = 0; c < kCopyRun; ++c) __builtin_nontemporal_store(v[c], dst + o + c * kWave);
   }
-  for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  // the elements past the last whole run
+  const int64_t t = int64_t(blockIdx.x) * kMeasureThreads + threadIdx.x;
+  for (int64_t i = runs * kCopyRun * kWave + t; i < n; i += waves * kWave)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 __global__ void __launch_bounds__(kMeasureThreads)
 read_kernel(const u32x4* __restrict__ src, int64_t n, uint32_t* __restrict__ out) {
   __shared__ uint32_t s[kMeasureThreads / kWave];
-  const int64_t stride = int64_t(gridDim.x) * kMeasureThreads;
-  int64_t i = int64_t(blockIdx.x) * kMeasureThreads + threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t waves = int64_t(gridDim.x) * (kMeasureThreads / kWave);
+  const int64_t wave = int64_t(blockIdx.x) * (kMeasureThreads / kWave) + threadIdx.x / kWave;
+  const int64_t runs = n / (int64_t(kReadRun) * kWave);
   uint32_t acc = 0;
-  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
-    u32x4 v[kUnroll];
+  for (int64_t r = wave; r < runs; r += waves) {
+    const u32x4* p = src + r * kReadRun * kWave + lane;
+    u32x4 v[kReadRun];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int c = 0; c < kReadRun; ++c) v[c] = __builtin_nontemporal_load(p + c * kWave);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int c = 0; c < kReadRun; ++c) acc ^= v[c].x ^ v[c].y ^ v[c].z ^ v[c].w;
   }
-  for (; i < n; i += stride) {
+  const int64_t t = int64_t(blockIdx.x) * kMeasureThreads + threadIdx.x;
+  for (int64_t i = runs * kReadRun * kWave + t; i < n; i += waves * kWave) {
     const u32x4 v = __builtin_nontemporal_load(src + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) acc ^= __shfl_xor(acc, d);
-  if ((threadIdx.x & (kWave - 1)) == 0) s[threadIdx.x / kWave] = acc;
+  if (lane == 0) s[threadIdx.x / kWave] = acc;
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t t = 0;
-    for (int ww = 0; ww < kMeasureThreads / kWave; ++ww) t ^= s[ww];
-    out[blockIdx.x] = t;
+    uint32_t x = 0;
+    for (int ww = 0; ww < kMeasureThreads / kWave; ++ww) x ^= s[ww];
+    out[blockIdx.x] = x;
   }
 }
 
@@ -183,8 +201,9 @@ mfma_random_kernel(int32_t iters, float* __restrict__ out) {
   if ((threadIdx.x & (kWave - 1)) == 0) out[blockIdx.x * (kMeasureThreads / kWave) + threadIdx.x / kWave] = s;
 }
 
-int measure_grid() {
-  const int g = device_cus() * 8;
+// workgroups per CU -> grid (at most 65536: the read and gather write one word per workgroup)
+int measure_grid(int per_cu) {
+  const int g = device_cus() * per_cu;
   return g < 65536 ? g : 65536;
 }
 
@@ -207,7 +226,7 @@ extern "C" int pa_measure_copy(void* dst, const void* src, size_t bytes, void* s
   const char* s = static_cast<const char*>(src);
   const char* d = static_cast<const char*>(dst);
   if (s < d + bytes && d < s + bytes) return fail(PA_ERR_INVALID, "pa_measure_copy: buffers overlap");
-  hipLaunchKernelGGL(copy_kernel, dim3(measure_grid()), dim3(kMeasureThreads), 0, static_cast<hipStream_t>(stream),
+  hipLaunchKernelGGL(copy_kernel, dim3(measure_grid(kCopyWgPerCu)), dim3(kMeasureThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), int64_t(bytes / 16));
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : fail(PA_ERR_HIP, "pa_measure_copy: launch failed: %s", hipGetErrorString(e));
@@ -216,7 +235,7 @@ extern "C" int pa_measure_copy(void* dst, const void* src, size_t bytes, void* s
 extern "C" int pa_measure_read(const void* src, size_t bytes, uint32_t* out, void* stream) {
   clear_error();
   if (int rc = check(src, out, bytes, "pa_measure_read")) return rc;
-  hipLaunchKernelGGL(read_kernel, dim3(measure_grid()), dim3(kMeasureThreads), 0, static_cast<hipStream_t>(stream),
+  hipLaunchKernelGGL(read_kernel, dim3(measure_grid(kReadWgPerCu)), dim3(kMeasureThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(src), int64_t(bytes / 16), out);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : fail(PA_ERR_HIP, "pa_measure_read: launch failed: %s", hipGetErrorString(e));
@@ -230,7 +249,7 @@ extern "C" int pa_measure_gather(const void* src, int64_t src_pages, const int32
     return fail(PA_ERR_INVALID, "pa_measure_gather: empty page list or buffer");
   if (page_bytes <= 0 || page_bytes % (kWave * 16) != 0)
     return fail(PA_ERR_INVALID, "pa_measure_gather: page_bytes must be a positive multiple of 1024");
-  hipLaunchKernelGGL(gather_kernel, dim3(measure_grid()), dim3(kMeasureThreads), 0, static_cast<hipStream_t>(stream),
+  hipLaunchKernelGGL(gather_kernel, dim3(measure_grid(8)), dim3(kMeasureThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const char*>(src), pages, npages, src_pages, page_bytes, out);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : fail(PA_ERR_HIP, "pa_measure_gather: launch failed: %s", hipGetErrorString(e));
