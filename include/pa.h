@@ -171,6 +171,29 @@ int pa_attention_noalloc(const void* q, const void* k_cache, const void* v_cache
                          int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
                          int32_t dtype, void* stream);
 
+/* Metadata the kernels had to clamp (a debug read-back).
+ *
+ * Metadata is trusted on the device, but no kernel indexes outside its
+ * buffers even when it is wrong: a block id outside [0, num_blocks) is read
+ * as the nearest valid block, and rows or a context inconsistent with
+ * num_tokens and max_blocks_per_seq are clamped.  Such a step's outputs are
+ * wrong.  Every kernel that clamps ORs a bit into a sticky flag word in the
+ * workspace header (no kernel ever clears it):
+ *   PA_FLAG_BLOCK_ID  a block id outside the pool was met;
+ *   PA_FLAG_ROWS      a sequence's query_start_loc / context_lens entries were
+ *                     inconsistent with the step (rows outside [0, num_tokens),
+ *                     a negative count or context, more keys than its block-table
+ *                     row holds) and were clamped.  seq_lens is not read on the
+ *                     device; pa_validate_metadata checks it.
+ * pa_attention_flags waits for `stream`, writes the word to *flags (host,
+ * may be NULL) and, if clear != 0, zeroes it (enqueued on `stream`).  The
+ * word is undefined in a fresh workspace: clear it once before the first step
+ * whose flags will be read.  workspace NULL means the current device's
+ * static workspace of pa_attention_noalloc (which starts at zero).  Not for
+ * use under graph capture (it synchronises and enqueues a memset). */
+enum { PA_FLAG_BLOCK_ID = 1, PA_FLAG_ROWS = 2 };
+int pa_attention_flags(const void* workspace, int32_t* flags, int32_t clear, void* stream);
+
 /* Check step metadata on host copies, O(num_tokens + num_seqs*max_blocks).
  *   seq_lens[i] == context_lens[i] + (query_start_loc[i+1]-query_start_loc[i]) >= 0,
  *   query_start_loc[0] == 0, non-decreasing, query_start_loc[num_seqs] == num_tokens,

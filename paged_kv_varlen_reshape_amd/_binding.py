@@ -30,6 +30,8 @@ PA_OPT_TARGET_ITEMS = 3
 PA_OPT_DECODE_BUFFERS = 4
 PA_OPT_DECODE_KERNEL = 5
 PA_OPT_VERIFY_ROWS = 6
+PA_FLAG_BLOCK_ID = 1
+PA_FLAG_ROWS = 2
 PA_K_RESHAPE, PA_K_PLAN, PA_K_CHUNK, PA_K_DECODE, PA_K_MERGE, PA_K_COUNT = range(6)
 KERNEL_NAMES = ["reshape_and_cache", "plan", "chunk_mfma", "decode", "split_merge"]  # PA_K_* kinds
 
@@ -45,6 +47,7 @@ SIGNATURES = {
                             _i32, _i64, _i32, _i32, _i32, _vp, _sz, _vp]),
     "pa_attention_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _i64, _i32, _i32, _i32, _vp]),
+    "pa_attention_flags": (_i32, [_vp, _pi32, _i32, _vp]),
     "pa_validate_metadata": (_i32, [_pi32, _pi32, _pi32, _pi32, _pi32, _i32, _i32, _i32, _i64, _i32]),
     "pa_last_error": (C.c_char_p, []),
     "pa_set_option": (_i32, [_i32, _i64]),
@@ -249,6 +252,19 @@ def pa_attention_noalloc(q, k_cache, v_cache, block_tables, seq_lens, query_star
                                       T if max_query_len is None else int(max_query_len), _dtype_code(q),
                                       _stream_handle(q.device)))
     return out
+
+
+def pa_attention_flags(workspace=None, clear: bool = False, device=None) -> int:
+    """Sticky PA_FLAG_* bits of metadata the kernels clamped, from a pa_attention
+    workspace (None: this device's pa_attention_noalloc workspace); waits for the
+    current stream.  clear=True zeroes the word afterwards."""
+    import torch
+
+    dev = workspace.device if workspace is not None else (device or torch.device("cuda", torch.cuda.current_device()))
+    out = C.c_int32(0)
+    ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    _check(lib().pa_attention_flags(ptr, C.byref(out), 1 if clear else 0, _stream_handle(dev)))
+    return int(out.value)
 
 
 def pa_measure_copy(dst, src) -> None:

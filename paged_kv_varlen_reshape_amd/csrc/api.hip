@@ -273,12 +273,22 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   // every decode workgroup plans the (few) rows itself
   a.self_plan = max_query_len <= 1 && bf16 && decode_uses_mfma(1) && num_tokens <= kSelfPlanRows &&
                 num_seqs <= kSelfPlanRows;
+  // a small step with chunks skips it too: the chunk kernel plans its tiles and
+  // the MFMA decode kernel the single-row sequences (short-query records need
+  // the plan kernel)
+  a.all_chunk = all_chunk ? 1 : 0;
+  a.chunk_self_plan = use_mfma && pa_args.verify_rows == 1 && decode_uses_mfma(1) && num_seqs <= kSelfPlanRows &&
+                      num_tokens <= kChunkSelfPlanTokens;
+  if (a.chunk_self_plan && !all_chunk) {
+    a.self_plan = 1;
+    a.self_skip_chunks = 1;
+  }
   a.fixed_units = pa_args.fixed_units;
   a.num_ranges = pa_args.num_ranges;
   a.max_len = pa_args.max_len;
 
   hipError_t e = hipSuccess;
-  if (!a.self_plan) {
+  if (!a.self_plan && !a.chunk_self_plan) {
     KernelTimer t(PA_K_PLAN, st);
     e = launch_plan(pa_args, w, st);
   }
@@ -323,6 +333,27 @@ extern "C" int pa_attention(const void* q, const void* k_cache, const void* v_ca
   return run_attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, context_lens, scale, out,
                        num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq,
                        max_query_len, dtype, workspace, stream, who);
+}
+
+extern "C" int pa_attention_flags(const void* workspace, int32_t* flags, int32_t clear, void* stream) {
+  clear_error();
+  static const char* who = "pa_attention_flags";
+  const void* ws = workspace ? workspace : noalloc_scratch(who);
+  if (!ws) return PA_ERR_HIP;
+  int32_t* word = static_cast<int32_t*>(const_cast<void*>(ws)) + H_FLAGS;  // the header opens the workspace
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (flags) {
+    int32_t v = 0;
+    hipError_t e = hipMemcpyAsync(&v, word, sizeof(v), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: read-back failed: %s", who, hipGetErrorString(e));
+    *flags = v;
+  }
+  if (clear) {
+    const hipError_t e = hipMemsetAsync(word, 0, sizeof(int32_t), st);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: clear failed: %s", who, hipGetErrorString(e));
+  }
+  return PA_OK;
 }
 
 extern "C" int pa_profile_enable(int32_t mask) {

@@ -150,6 +150,9 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
   __shared__ __attribute__((aligned(16))) char s_v0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char s_v1[C::TILE_BYTES];
   __shared__ int s_item;
+  __shared__ int s_tbase[kSelfPlanRows + 1];  // self-planned steps: first tile of each sequence,
+  __shared__ int s_qsl[kSelfPlanRows + 1];    //   its query_start_loc entries
+  __shared__ int s_ctx[kSelfPlanRows];        //   and its context_lens entry
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -185,7 +188,65 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
     off_v[j] = uint32_t(row * RB + 16 * (dma_chunk ^ (v_swz(row) & (CH - 1))));
   }
 
-  const int n_items = w.hdr[H_TILES] * a.hkv;
+  // A small step may be planned here instead of by the plan kernel: every
+  // workgroup counts the tiles of each sequence (the same routing and clamping
+  // as the plan) and keeps their prefix sum in LDS; tiles stay in sequence
+  // order and every workgroup takes its queue positions in a fixed stride, so
+  // nothing depends on counters or a sorted list in the workspace.
+  int n_items;
+  if (a.chunk_self_plan) {
+    constexpr int SPT = kSelfPlanRows / kThreads;  // sequences per thread
+    int cnt[SPT], tot = 0;
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int i = tid * SPT + k;
+      int q = 0;
+      if (i < a.num_seqs) {
+        const int r0 = a.qsl[i], r1 = a.qsl[i + 1], cr = a.ctx[i];
+        s_qsl[i] = r0;  // kept for the items' metadata (meta_stage2)
+        s_ctx[i] = cr;
+        if (i == a.num_seqs - 1) s_qsl[i + 1] = r1;
+        q = int(min(int64_t(max(r1 - r0, 0)), int64_t(a.num_tokens) - r0));
+        if (r0 < 0 || r0 >= a.num_tokens) q = 0;
+        const int c = max(cr, 0);
+        if (int64_t(c) + q > a.max_len) q = c >= a.max_len ? 0 : a.max_len - c;
+        if (blockIdx.x == 0) {  // metadata clamped above: sticky flag (once, not per workgroup)
+          const int f = rows_flag(r0, r1, cr, a.num_tokens, a.max_len);
+          if (f) atomicOr(&w.hdr[H_FLAGS], f);
+        }
+      }
+      cnt[k] = q > (a.all_chunk ? 0 : 1) ? (q + TQ - 1) / TQ : 0;  // a chunk sequence's tiles
+      tot += cnt[k];
+    }
+    // exclusive scan of the per-thread tile counts over the workgroup
+    int incl = tot;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int x = __shfl_up(incl, d);
+      if (lane >= d) incl += x;
+    }
+    if (lane == kWave - 1) s_tbase[kSelfPlanRows - kThreads / kWave + wave] = incl;  // wave totals, scratch
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int ww = 0; ww < kThreads / kWave; ++ww) {
+      const int t = s_tbase[kSelfPlanRows - kThreads / kWave + ww];
+      base += ww < wave ? t : 0;
+      total += t;
+    }
+    __syncthreads();  // the wave totals are read before the table overwrites them
+    int run = base + incl - tot;
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      s_tbase[tid * SPT + k] = run;
+      run += cnt[k];
+    }
+    if (tid == 0) s_tbase[kSelfPlanRows] = total;
+    __syncthreads();
+    n_items = __builtin_amdgcn_readfirstlane(total) * a.hkv;
+  } else {
+    n_items = w.hdr[H_TILES] * a.hkv;
+  }
   // Items are (tile, kv head) pairs, item = tile * hkv + kv head, tiles longest
   // first.  Tiles of one sequence and kv head re-read the same K/V prefix, so
   // when the kv heads split evenly over the XCDs each XCD gets a queue of its
@@ -226,14 +287,33 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
   auto meta_stage1 = [&](int it, Meta& mt) __attribute__((always_inline)) {
     if (it >= n_items) return;
     const int tl = __builtin_amdgcn_readfirstlane(it / a.hkv);
-    mt.seq = ctiles[2 * tl];
-    mt.t0 = ctiles[2 * tl + 1];
+    if (a.chunk_self_plan) {
+      // the last sequence whose first tile is at or before tl (sequences
+      // without tiles share their successor's first tile and are passed over)
+      int lo = 0, hi = a.num_seqs;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_tbase[mid] <= tl) lo = mid;
+        else hi = mid;
+      }
+      mt.seq = __builtin_amdgcn_readfirstlane(lo);
+      mt.t0 = __builtin_amdgcn_readfirstlane((tl - s_tbase[lo]) * TQ);
+    } else {
+      mt.seq = ctiles[2 * tl];
+      mt.t0 = ctiles[2 * tl + 1];
+    }
   };
   auto meta_stage2 = [&](int it, Meta& mt) __attribute__((always_inline)) {
     if (it >= n_items) return;
-    mt.r0 = cqsl[mt.seq];
-    mt.qend = cqsl[mt.seq + 1];
-    mt.ctx = cctx[mt.seq];
+    if (a.chunk_self_plan) {  // kept in LDS by the self-plan
+      mt.r0 = __builtin_amdgcn_readfirstlane(s_qsl[mt.seq]);
+      mt.qend = __builtin_amdgcn_readfirstlane(s_qsl[mt.seq + 1]);
+      mt.ctx = __builtin_amdgcn_readfirstlane(s_ctx[mt.seq]);
+    } else {
+      mt.r0 = cqsl[mt.seq];
+      mt.qend = cqsl[mt.seq + 1];
+      mt.ctx = cctx[mt.seq];
+    }
   };
   // the plan clamped the rows it tiled the same way: nothing may index
   // outside q, out or the block-table row even with inconsistent metadata
@@ -249,7 +329,9 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
     if (wave * kBlock < kv_end_n) mt.blk0 = cbt[int64_t(mt.seq) * a.mbps + wave];
   };
 
-  int item = queue_item(int(blockIdx.x) / (xcd_queues ? kXcdQueues : 1));
+  bool blk_bad = false;  // a block id outside the pool was clamped (reported at the end)
+  int qpos = int(blockIdx.x) / (xcd_queues ? kXcdQueues : 1);  // queue position of the current item
+  int item = queue_item(qpos);
   Meta cur{};
   meta_stage1(item, cur);
   meta_stage2(item, cur);
@@ -264,7 +346,9 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
     Meta nxt{};
     auto handover = [&]() __attribute__((always_inline)) {
       if (phase == 0) {
-        if (tid == 0) claimed = queue_item(q_wgs + atomicAdd(&w.hdr[H_QUEUE + xq], 1));
+        // self-planned: the next position in this workgroup's fixed stride
+        if (tid == 0)
+          claimed = queue_item(a.chunk_self_plan ? qpos + q_wgs : q_wgs + atomicAdd(&w.hdr[H_QUEUE + xq], 1));
       } else if (phase == 1) {
         if (tid == 0) s_item = claimed;
       } else if (phase == 2) {
@@ -327,6 +411,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
       if (kt * 4 + wave >= n_pages) return;
       raw = __builtin_amdgcn_readfirstlane(raw);
       const int32_t blk = raw < 0 ? 0 : (raw >= a.nb ? int32_t(a.nb - 1) : raw);  // never leave the pool
+      blk_bad |= blk != raw;
       const int64_t page = (int64_t(blk) * a.hkv + kvh) * page_stride;
       // one buffer descriptor per page: the per-lane offsets stay 32-bit and
       // a copy can never read past the page
@@ -531,7 +616,9 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
     __syncthreads();
     item = next;
     cur = nxt;
+    qpos += q_wgs;
   }
+  if (blk_bad && lane == 0) atomicOr(&w.hdr[H_FLAGS], PA_FLAG_BLOCK_ID);
 }
 
 template <int D, int G>

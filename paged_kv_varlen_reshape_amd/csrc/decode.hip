@@ -195,6 +195,7 @@ decode_streamk_kernel(AttnArgs a, Workspace w) {
   const char* kbase = static_cast<const char*>(a.kc);
   const char* vbase = static_cast<const char*>(a.vc);
 
+  bool blk_bad = false;  // a block id outside the pool was clamped (reported at the end)
   for (int g = gwave; g < nranges; g += nwaves) {
     int64_t x = g * per;
     const int64_t x_end = min(x + per, units);
@@ -235,6 +236,7 @@ decode_streamk_kernel(AttnArgs a, Workspace w) {
         const int j = j0 + lane;
         const int32_t b = j < n ? btrow[j] : 0;
         ids = b < 0 ? 0 : (b >= a.nb ? int32_t(a.nb - 1) : b);  // never leave the pool
+        blk_bad |= ids != b;
       };
       auto page_off = [&](int j) -> int64_t {
         const int32_t b = __builtin_amdgcn_readlane(ids, j & (kWave - 1));
@@ -317,6 +319,7 @@ decode_streamk_kernel(AttnArgs a, Workspace w) {
       }
     }
   }
+  if (__any(blk_bad) && lane == 0) atomicOr(&w.hdr[H_FLAGS], PA_FLAG_BLOCK_ID);
 }
 
 // split_merge: (record, kv head) pairs cut by range boundaries.  Range g's

@@ -151,7 +151,9 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
   const char* kbase = static_cast<const char*>(a.kc);
   const char* vbase = static_cast<const char*>(a.vc);
 
-  // A small decode-only step is planned here, by every workgroup for itself,
+  // A small step's row-wise rows (every row of a decode-only step; the
+  // single-row sequences of a mixed one, whose chunks the chunk kernel plans
+  // for itself) are planned here, by every workgroup for itself,
   // instead of by the plan kernel: the row records and their first units go
   // to LDS (workgroup 0 also stores them, and the step's header, for the
   // merge), and each range finds its first row by binary search.  Same
@@ -176,6 +178,11 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
         if (r0 < 0 || r0 >= a.num_tokens) q = 0;
         c = max(a.ctx[i], 0);
         if (int64_t(c) + q > a.max_len) q = c >= a.max_len ? 0 : a.max_len - c;
+        if (a.self_skip_chunks && q > 1) q = 0;  // a chunk: the chunk kernel's rows
+        if (blockIdx.x == 0) {  // metadata clamped above: sticky flag (once, not per workgroup)
+          const int f = rows_flag(r0, a.qsl[i + 1], a.ctx[i], a.num_tokens, a.max_len);
+          if (f) atomicOr(&w.hdr[H_FLAGS], f);
+        }
       }
       r0s[k] = r0;
       qs[k] = q;
@@ -241,6 +248,7 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
       }
     }
   }
+  bool blk_bad = false;  // a block id outside the pool was clamped (reported at the end)
   auto rec_at = [&](int r) __attribute__((always_inline)) -> int4 { return SELF ? s_rec[r] : w.rows[r]; };
   auto base_at = [&](int r) __attribute__((always_inline)) -> int64_t { return SELF ? s_base[r] : w.rows_base[r]; };
 
@@ -349,6 +357,7 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
         const int32_t braw = __builtin_amdgcn_readlane(ids, f & (kWave - 1));
         const int kh = __builtin_amdgcn_readlane(khs, f & (kWave - 1));
         const int32_t b = braw < 0 ? 0 : (braw >= a.nb ? int32_t(a.nb - 1) : braw);  // never leave the pool
+        blk_bad |= b != braw;
         const int64_t pb = (int64_t(b) * hkv + kh) * PAGE;
 #pragma unroll
         for (int ii = 0; ii < IPG; ++ii) {
@@ -568,6 +577,7 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
         const int j = j0 + lane;
         const int32_t b = j < n ? btrow[j] : 0;
         ids = b < 0 ? 0 : (b >= a.nb ? int32_t(a.nb - 1) : b);  // never leave the pool
+        blk_bad |= ids != b;
       };
       auto page_base = [&](int j) -> int64_t {
         const int32_t b = __builtin_amdgcn_readlane(ids, j & (kWave - 1));
@@ -685,6 +695,7 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
       }
     }
   }
+  if (__any(blk_bad) && lane == 0) atomicOr(&w.hdr[H_FLAGS], PA_FLAG_BLOCK_ID);
 }
 
 template <int D, int G, int NBUF>

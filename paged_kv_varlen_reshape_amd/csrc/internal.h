@@ -32,6 +32,7 @@ enum PlanHeader : int {
   H_ROWS = 0,     // row-wise rows
   H_TILES = 1,    // query tiles of the MFMA chunk kernel
   H_RANGES = 2,   // decode ranges (one wavefront each, in stream order)
+  H_FLAGS = 3,    // sticky PA_FLAG_* bits: metadata a kernel had to clamp (never cleared by a kernel)
   H_QUEUE = 8,    // kXcdQueues dynamic work counters of the chunk kernel (words 8..15)
   H64 = 16,       // int64 words follow
   H64_UNITS = 0,  // (row, kv head, page) units of all row-wise rows
@@ -100,6 +101,14 @@ struct PlanArgs {
 };
 hipError_t launch_plan(const PlanArgs& a, const Workspace& w, hipStream_t st);
 
+// PA_FLAG_ROWS if the rows of one sequence (query_start_loc r0..r1, cached
+// context ctx) are not consistent with the step, i.e. if the plans clamp them:
+// rows outside [0, num_tokens), a negative count or context, or more keys than
+// the block-table row holds.
+__device__ __forceinline__ int rows_flag(int64_t r0, int64_t r1, int64_t ctx, int64_t num_tokens, int64_t max_len) {
+  return (r1 < r0 || r0 < 0 || r1 > num_tokens || ctx < 0 || ctx + (r1 - r0) > max_len) ? PA_FLAG_ROWS : 0;
+}
+
 // Units (pages of 16 keys) of the rows whose key counts are 1..n:
 // sum over p = 1..n of ceil(p / 16).
 __device__ __forceinline__ int64_t pages_upto(int64_t n) {
@@ -118,9 +127,13 @@ __device__ __forceinline__ int4 cut_record(int64_t f, int64_t pages, int64_t per
   return make_int4(tok, kvh | (nq << 16), int(g0), int(2 * (g1 - g0 + 1)) | (f != g0 * per ? 1 : 0));
 }
 
-// Most rows (and sequences) of a decode-only step that the MFMA decode kernel
-// plans by itself, without the plan kernel.
+// Most rows (and sequences) of a step that the MFMA decode kernel plans by
+// itself, without the plan kernel; also the most sequences of a step the chunk
+// kernel plans by itself.
 constexpr int kSelfPlanRows = 512;
+// Most query tokens of a step the chunk kernel plans by itself (its tiles then
+// run in sequence order, not longest first).
+constexpr int kChunkSelfPlanTokens = 2048;
 
 struct AttnArgs {
   const void* q;
@@ -144,7 +157,10 @@ struct AttnArgs {
   int64_t nb;
   int32_t bf16;
   int32_t merge_rows;  // most query rows of one row-wise record this step (the plan's verify_rows)
-  int32_t self_plan;   // 1: decode-only step the MFMA decode kernel plans by itself (no plan kernel)
+  int32_t self_plan;   // 1: the MFMA decode kernel plans the step's row-wise rows by itself (no plan kernel)
+  int32_t self_skip_chunks;  // with self_plan: sequences with more than one query row belong to the chunk kernel
+  int32_t chunk_self_plan;   // 1: small step the chunk kernel plans by itself (no plan kernel)
+  int32_t all_chunk;         // 1: every sequence with query rows goes to the chunk kernel (the plan's all_chunk)
   int32_t fixed_units, num_ranges, max_len;  // the plan's range parameters, for self_plan
 };
 hipError_t launch_decode(const AttnArgs& a, const Workspace& w, int group, hipStream_t st);
@@ -164,6 +180,9 @@ bool chunk_supported(int head_dim, int group, int bf16);
 int chunk_tile_rows(int group);
 
 int device_cus();
+// The current device's static workspace of pa_attention_noalloc (nullptr, with the
+// error set, if it cannot be found).
+void* noalloc_scratch(const char* who);
 
 // pa_attention's argument checks (PA_OK, or the error it reports for `who`) and
 // its launch sequence on an already checked call with a workspace of at least

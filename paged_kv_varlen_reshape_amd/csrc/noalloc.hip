@@ -47,6 +47,9 @@ void* scratch_ptr(const char* who) {
 }
 
 }  // namespace
+
+void* noalloc_scratch(const char* who) { return scratch_ptr(who); }
+
 }  // namespace pa
 
 using namespace pa;

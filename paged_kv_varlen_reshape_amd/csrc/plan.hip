@@ -116,11 +116,15 @@ plan_kernel(PlanArgs a, Workspace w) {
   const int64_t m = (int64_t(a.num_seqs) + kPlanThreads - 1) / kPlanThreads;
   const int64_t i0 = min(int64_t(tid) * m, int64_t(a.num_seqs)), i1 = min(i0 + m, int64_t(a.num_seqs));
   int64_t ntile = 0, nrow = 0, nunit = 0;
+  int flags = 0;
   for (int64_t ib = i0; ib < i1; ib += kSeqBatch) {
 #pragma unroll
     for (int c = 0; c < kSeqBatch; ++c)
       seq_counts(seq_info(a, ib + c, ib + c < i1), a.tile_rows, hkv, ntile, nrow, nunit);
   }
+  for (int64_t i = i0; i < i1; ++i)  // metadata the rows above were clamped against (sticky flag)
+    flags |= rows_flag(a.qsl[i], a.qsl[i + 1], a.ctx[i], a.num_tokens, a.max_len);
+  if (flags) atomicOr(&w.hdr[H_FLAGS], flags);
   int64_t off_tr, off_u, tot_tr, tot_u;
   block_exclusive_scan2((ntile << 32) | nrow, nunit, &off_tr, &off_u, &tot_tr, &tot_u, sh);
   int64_t tiles = tot_tr >> 32, rows = tot_tr & 0xFFFFFFFFll;
