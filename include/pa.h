@@ -223,11 +223,15 @@ enum {
                                 2); 0 or a value the kernel does not take: automatic */
   PA_OPT_DECODE_KERNEL = 5,  /* row-wise rows of bf16 steps: 0 automatic (MFMA), 1 VALU kernel,
                                 2 MFMA kernel; float32 steps always take the VALU kernel */
-  PA_OPT_VERIFY_ROWS = 6     /* bf16 steps with the MFMA row-wise kernel: a sequence with 2..n
+  PA_OPT_VERIFY_ROWS = 6,    /* bf16 steps with the MFMA row-wise kernel: a sequence with 2..n
                                 query rows (a short query, e.g. speculative-decoding verification)
                                 is one row-wise work item whose rows share every K/V page instead
                                 of chunk tiles; n = this value capped at 16 / (q heads per kv
                                 head); 0 (automatic) and 1: off.  Changes the workspace size */
+  PA_OPT_CHUNK_KERNEL = 7    /* bf16 chunk rows: 0 (automatic) and 1: the four-wavefront chunk
+                                kernel; 2: the eight-wavefront kernel (two groups alternating
+                                products and softmax) for every step with chunk rows, the plan
+                                kernel then planning every step.  Both compute the same rows */
 };
 int pa_set_option(int32_t option, int64_t value);
 int64_t pa_get_option(int32_t option);

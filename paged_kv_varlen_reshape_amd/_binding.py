@@ -30,6 +30,7 @@ PA_OPT_TARGET_ITEMS = 3
 PA_OPT_DECODE_BUFFERS = 4
 PA_OPT_DECODE_KERNEL = 5
 PA_OPT_VERIFY_ROWS = 6
+PA_OPT_CHUNK_KERNEL = 7
 PA_FLAG_BLOCK_ID = 1
 PA_FLAG_ROWS = 2
 PA_K_RESHAPE, PA_K_PLAN, PA_K_CHUNK, PA_K_DECODE, PA_K_MERGE, PA_K_COUNT = range(6)

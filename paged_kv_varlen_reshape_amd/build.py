@@ -33,10 +33,14 @@ COMMON = ["-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", INCLUDE,
 # V rows past the sequence are zeroed, and the factor the raw scores are
 # multiplied by is positive, the host having folded a negative or zero scale
 # into Q), so max/min need no NaN canonicalisation
-FILE_FLAGS = {"chunk.hip": ["-fno-honor-nans"]}
+FILE_FLAGS = {"chunk.hip": ["-fno-honor-nans"],
+              # the work-queue claim is one lane's atomic whose result is used two steps
+              # later; the atomic optimizer would rewrite it into a wave-wide read-back
+              # that waits for it (and for every copy in flight) at once
+              "chunk_pp.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 SOURCES = ["errors.cpp", "pool.cpp", "validate.cpp", "api.hip", "reshape.hip", "plan.hip",
-           "decode.hip", "decode_mfma.hip", "chunk.hip", "measure.hip", "noalloc.hip"]
+           "decode.hip", "decode_mfma.hip", "chunk.hip", "chunk_pp.hip", "measure.hip", "noalloc.hip"]
 
 
 def _compile(src: str, opt: list[str]) -> str:

@@ -7,6 +7,7 @@
 #include <vector>
 
 #include "internal.h"
+#include "chunk_pp.h"
 
 namespace pa {
 
@@ -278,11 +279,14 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   // the plan kernel)
   a.all_chunk = all_chunk ? 1 : 0;
   a.chunk_self_plan = use_mfma && pa_args.verify_rows == 1 && decode_uses_mfma(1) && num_seqs <= kSelfPlanRows &&
-                      num_tokens <= kChunkSelfPlanTokens;
+                      num_tokens <= kChunkSelfPlanTokens && option(PA_OPT_CHUNK_KERNEL) != 2;
   if (a.chunk_self_plan && !all_chunk) {
     a.self_plan = 1;
     a.self_skip_chunks = 1;
   }
+  // on request, the eight-wavefront chunk kernel (its tiles are twice as long)
+  const bool chunk_pp = use_mfma && !a.chunk_self_plan && chunk_pp_selected(head_dim, group, bf16 ? 1 : 0, max_query_len);
+  if (chunk_pp) pa_args.tile_rows = chunk_pp_tile_rows(group);
   a.fixed_units = pa_args.fixed_units;
   a.num_ranges = pa_args.num_ranges;
   a.max_len = pa_args.max_len;
@@ -294,7 +298,7 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   }
   if (e == hipSuccess && use_mfma) {
     KernelTimer t(PA_K_CHUNK, st);
-    e = launch_chunk(a, w, group, st);
+    e = chunk_pp ? launch_chunk_pp(a, w, group, st) : launch_chunk(a, w, group, st);
   }
   if (e == hipSuccess && !all_chunk) {
     KernelTimer t(PA_K_DECODE, st);

@@ -15,6 +15,7 @@ std::atomic<int64_t> g_target_items{0};
 std::atomic<int64_t> g_decode_buffers{0};
 std::atomic<int64_t> g_decode_kernel{0};
 std::atomic<int64_t> g_verify_rows{0};
+std::atomic<int64_t> g_chunk_kernel{0};
 }  // namespace
 
 int fail(int code, const char* fmt, ...) {
@@ -37,6 +38,7 @@ int64_t option(int32_t id) {
     case PA_OPT_DECODE_BUFFERS: return g_decode_buffers.load();
     case PA_OPT_DECODE_KERNEL: return g_decode_kernel.load();
     case PA_OPT_VERIFY_ROWS: return g_verify_rows.load();
+    case PA_OPT_CHUNK_KERNEL: return g_chunk_kernel.load();
     default: return -1;
   }
 }
@@ -70,6 +72,10 @@ extern "C" int pa_set_option(int32_t id, int64_t value) {
     case PA_OPT_VERIFY_ROWS:
       if (value < 0 || value > 16) return pa::fail(PA_ERR_INVALID, "PA_OPT_VERIFY_ROWS takes 0..16");
       pa::g_verify_rows = value;
+      return PA_OK;
+    case PA_OPT_CHUNK_KERNEL:
+      if (value < 0 || value > 2) return pa::fail(PA_ERR_INVALID, "PA_OPT_CHUNK_KERNEL takes 0, 1 or 2");
+      pa::g_chunk_kernel = value;
       return PA_OK;
     default:
       return pa::fail(PA_ERR_INVALID, "unknown option %d", id);

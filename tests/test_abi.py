@@ -111,7 +111,8 @@ def test_workspace_size_is_deterministic_and_grows():
 
 def test_options_roundtrip_and_errors():
     for opt, val in ((pk.PA_OPT_FORCE_ROWWISE, 1), (pk.PA_OPT_SPLIT_TOKENS, 64), (pk.PA_OPT_TARGET_ITEMS, 100),
-                     (pk.PA_OPT_DECODE_BUFFERS, 2), (pk.PA_OPT_DECODE_KERNEL, 1), (pk.PA_OPT_VERIFY_ROWS, 3)):
+                     (pk.PA_OPT_DECODE_BUFFERS, 2), (pk.PA_OPT_DECODE_KERNEL, 1), (pk.PA_OPT_VERIFY_ROWS, 3),
+                     (pk.PA_OPT_CHUNK_KERNEL, 2)):
         old = pk.pa_get_option(opt)
         pk.pa_set_option(opt, val)
         assert pk.pa_get_option(opt) == val

@@ -45,6 +45,7 @@ def _reset_options():
     pk.pa_set_option(pk.PA_OPT_DECODE_BUFFERS, 0)
     pk.pa_set_option(pk.PA_OPT_DECODE_KERNEL, 0)
     pk.pa_set_option(pk.PA_OPT_VERIFY_ROWS, 0)
+    pk.pa_set_option(pk.PA_OPT_CHUNK_KERNEL, 0)
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3])

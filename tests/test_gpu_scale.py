@@ -6,7 +6,8 @@ scale applied before the maximum (Inside vLLM summary, techfeed.io, section
 positions and a mask; where the scale sits is this repository's reading, the
 same one the oracle takes).  The library accepts any finite scale, so a zero,
 a negative and a large one must come out right on each kernel:
-  * the MFMA chunk kernel (rows of multi-row sequences, bf16),
+  * the MFMA chunk kernels (rows of multi-row sequences, bf16: four
+    wavefronts per workgroup, and eight in two alternating groups),
   * the MFMA row-wise decode kernel (decode rows, bf16; every row when forced),
   * the VALU row-wise kernel (float32 steps; bf16 rows on request).
 At scale 0 every weight is equal, so each row is also checked against the
@@ -35,6 +36,7 @@ def _reset_options():
     pk.pa_set_option(pk.PA_OPT_FORCE_ROWWISE, 0)
     pk.pa_set_option(pk.PA_OPT_DECODE_KERNEL, 0)
     pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, 0)
+    pk.pa_set_option(pk.PA_OPT_CHUNK_KERNEL, 0)
 
 
 def _mixed_spec(dtype, d, g, seed):
@@ -65,12 +67,13 @@ def _mean_of_visible_v(spec):
     return np.stack(rows)
 
 
-# (kernel routing name, FORCE_ROWWISE, DECODE_KERNEL): which kernels compute the rows
+# (kernel routing name, FORCE_ROWWISE, DECODE_KERNEL, CHUNK_KERNEL): which kernels compute the rows
 ROUTES = {
-    "chunk+decode_mfma": (0, 2),
-    "chunk+decode_valu": (0, 1),
-    "all_decode_mfma": (1, 2),
-    "all_decode_valu": (1, 1),
+    "chunk+decode_mfma": (0, 2, 1),
+    "chunk_pp+decode_mfma": (0, 2, 2),
+    "chunk+decode_valu": (0, 1, 1),
+    "all_decode_mfma": (1, 2, 0),
+    "all_decode_valu": (1, 1, 0),
 }
 
 
@@ -78,12 +81,13 @@ ROUTES = {
 @pytest.mark.parametrize("route", list(ROUTES))
 def test_bf16_scales_every_kernel(route, d, g):
     spec = _mixed_spec("bf16", d, g, 600 + d + g)
-    rowwise, kernel = ROUTES[route]
+    rowwise, kernel, chunk = ROUTES[route]
     print(f"scales bf16 route={route} d={d} g={g}", flush=True)
     ds = build_device_step(spec)
     ds.reshape()
     pk.pa_set_option(pk.PA_OPT_FORCE_ROWWISE, rowwise)
     pk.pa_set_option(pk.PA_OPT_DECODE_KERNEL, kernel)
+    pk.pa_set_option(pk.PA_OPT_CHUNK_KERNEL, chunk)
     for scale in (0.0, -1.0 / math.sqrt(d), -0.6, 2.0, 8.0):
         for split in (0, 48):
             pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, split)
