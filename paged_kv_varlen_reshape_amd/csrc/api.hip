@@ -278,8 +278,14 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   // the MFMA decode kernel the single-row sequences (short-query records need
   // the plan kernel)
   a.all_chunk = all_chunk ? 1 : 0;
-  a.chunk_self_plan = use_mfma && pa_args.verify_rows == 1 && decode_uses_mfma(1) && num_seqs <= kSelfPlanRows &&
-                      num_tokens <= kChunkSelfPlanTokens && option(PA_OPT_CHUNK_KERNEL) != 2;
+  {
+    const int64_t tiles_bound = use_mfma ? int64_t(num_tokens) / chunk_tile_rows(group) + num_seqs : 0;
+    const bool sortable = num_seqs <= kChunkSortSeqs && tiles_bound <= kChunkSortTiles &&
+                          tiles_bound * num_seqs <= kChunkSortPairs;
+    const bool can = use_mfma && pa_args.verify_rows == 1 && decode_uses_mfma(1) && num_seqs <= kSelfPlanRows &&
+                     option(PA_OPT_CHUNK_KERNEL) != 2;
+    a.chunk_self_plan = can && (num_tokens <= kChunkSelfPlanTokens || (all_chunk && sortable)) ? (sortable ? 2 : 1) : 0;
+  }
   if (a.chunk_self_plan && !all_chunk) {
     a.self_plan = 1;
     a.self_skip_chunks = 1;

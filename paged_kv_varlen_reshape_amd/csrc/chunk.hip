@@ -152,7 +152,9 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
   __shared__ int s_item;
   __shared__ int s_tbase[kSelfPlanRows + 1];  // self-planned steps: first tile of each sequence,
   __shared__ int s_qsl[kSelfPlanRows + 1];    //   its query_start_loc entries
-  __shared__ int s_ctx[kSelfPlanRows];        //   and its context_lens entry
+  __shared__ int s_ctx[kSelfPlanRows];        //   and its context_lens entry,
+  __shared__ int s_q[kSelfPlanRows];          //   its chunk rows (clamped; 0 if none)
+  __shared__ int s_order[kChunkSortTiles];    //   and, longest first, the tiles in sequence order
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -190,10 +192,12 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
 
   // A small step may be planned here instead of by the plan kernel: every
   // workgroup counts the tiles of each sequence (the same routing and clamping
-  // as the plan) and keeps their prefix sum in LDS; tiles stay in sequence
-  // order and every workgroup takes its queue positions in a fixed stride, so
-  // nothing depends on counters or a sorted list in the workspace.
+  // as the plan) and keeps their prefix sum in LDS.  With chunk_self_plan = 2
+  // it also ranks the tiles longest first (below); every workgroup then takes
+  // its queue positions in fixed rounds, so nothing depends on counters or a
+  // list in the workspace.
   int n_items;
+  bool sorted = false;
   if (a.chunk_self_plan) {
     constexpr int SPT = kSelfPlanRows / kThreads;  // sequences per thread
     int cnt[SPT], tot = 0;
@@ -216,6 +220,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
         }
       }
       cnt[k] = q > (a.all_chunk ? 0 : 1) ? (q + TQ - 1) / TQ : 0;  // a chunk sequence's tiles
+      if (i < a.num_seqs) s_q[i] = cnt[k] > 0 ? q : 0;
       tot += cnt[k];
     }
     // exclusive scan of the per-thread tile counts over the workgroup
@@ -243,7 +248,46 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
     }
     if (tid == 0) s_tbase[kSelfPlanRows] = total;
     __syncthreads();
-    n_items = __builtin_amdgcn_readfirstlane(total) * a.hkv;
+    total = __builtin_amdgcn_readfirstlane(total);
+    n_items = total * a.hkv;
+
+    // Longest first, without a sort: a tile's rank is the number of tiles that
+    // see more keys (its last row's), or as many with a lower index.  Within a
+    // sequence (c cached tokens, q chunk rows) tile t sees c + min(q, TQ(t+1))
+    // keys, strictly increasing in t, so each other sequence's count is a
+    // closed form.  Every workgroup computes the same ranks.
+    // (only when the items take more than one round of the grid: in one round
+    // every workgroup takes one item and the order changes nothing)
+    sorted = a.chunk_self_plan == 2 && total <= kChunkSortTiles && a.num_seqs <= kChunkSortSeqs &&
+             n_items > int(gridDim.x);
+    if (sorted) {
+      for (int i = tid; i < total; i += kThreads) {
+        int lo = 0, hi = a.num_seqs;  // the last sequence whose first tile is at or before i
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_tbase[mid] <= i) lo = mid;
+          else hi = mid;
+        }
+        const int keys = max(s_ctx[lo], 0) + min(s_q[lo], TQ * (i - s_tbase[lo] + 1));
+        int rank = 0;
+        for (int s2 = 0; s2 < a.num_seqs; ++s2) {
+          const int first = s_tbase[s2], n2 = s_tbase[s2 + 1] - first;
+          if (n2 == 0) continue;
+          const int f = keys - max(s_ctx[s2], 0), q2 = s_q[s2];
+          if (f < 0) {  // every tile of s2 sees more keys
+            rank += n2;
+            continue;
+          }
+          // full tiles t2 < n2 - 1 see c2 + TQ(t2+1) keys, the last c2 + q2
+          rank += max(0, n2 - 1 - f / TQ) + (q2 > f ? 1 : 0);
+          // an equal tile with a lower index
+          const int t_eq = (f % TQ == 0 && f / TQ - 1 < n2 - 1) ? f / TQ - 1 : (q2 == f ? n2 - 1 : -1);
+          if (t_eq >= 0 && first + t_eq < i) ++rank;
+        }
+        s_order[rank] = i;
+      }
+      __syncthreads();
+    }
   } else {
     n_items = w.hdr[H_TILES] * a.hkv;
   }
@@ -288,16 +332,17 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
     if (it >= n_items) return;
     const int tl = __builtin_amdgcn_readfirstlane(it / a.hkv);
     if (a.chunk_self_plan) {
-      // the last sequence whose first tile is at or before tl (sequences
+      const int ti = sorted ? __builtin_amdgcn_readfirstlane(s_order[tl]) : tl;  // tile in sequence order
+      // the last sequence whose first tile is at or before it (sequences
       // without tiles share their successor's first tile and are passed over)
       int lo = 0, hi = a.num_seqs;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (s_tbase[mid] <= tl) lo = mid;
+        if (s_tbase[mid] <= ti) lo = mid;
         else hi = mid;
       }
       mt.seq = __builtin_amdgcn_readfirstlane(lo);
-      mt.t0 = __builtin_amdgcn_readfirstlane((tl - s_tbase[lo]) * TQ);
+      mt.t0 = __builtin_amdgcn_readfirstlane((ti - s_tbase[lo]) * TQ);
     } else {
       mt.seq = ctiles[2 * tl];
       mt.t0 = ctiles[2 * tl + 1];
@@ -330,8 +375,17 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
   };
 
   bool blk_bad = false;  // a block id outside the pool was clamped (reported at the end)
-  int qpos = int(blockIdx.x) / (xcd_queues ? kXcdQueues : 1);  // queue position of the current item
-  int item = queue_item(qpos);
+  // Self-planned steps take queue positions in rounds: round r covers
+  // positions r * q_wgs .. (r + 1) * q_wgs - 1, one per workgroup of the queue,
+  // in workgroup order on even rounds and, with longest-first tiles, in
+  // reverse order on odd rounds (so the workgroup with the longest first item
+  // gets the shortest second one).
+  const int qu = int(blockIdx.x) / (xcd_queues ? kXcdQueues : 1);  // this workgroup's index in its queue
+  int rnd = 0;
+  auto round_pos = [&](int r) __attribute__((always_inline)) -> int {
+    return r * q_wgs + ((sorted && (r & 1)) ? q_wgs - 1 - qu : qu);
+  };
+  int item = queue_item(round_pos(0));
   Meta cur{};
   meta_stage1(item, cur);
   meta_stage2(item, cur);
@@ -348,7 +402,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
       if (phase == 0) {
         // self-planned: the next position in this workgroup's fixed stride
         if (tid == 0)
-          claimed = queue_item(a.chunk_self_plan ? qpos + q_wgs : q_wgs + atomicAdd(&w.hdr[H_QUEUE + xq], 1));
+          claimed = queue_item(a.chunk_self_plan ? round_pos(rnd + 1) : q_wgs + atomicAdd(&w.hdr[H_QUEUE + xq], 1));
       } else if (phase == 1) {
         if (tid == 0) s_item = claimed;
       } else if (phase == 2) {
@@ -616,7 +670,7 @@ chunk_mfma_kernel(AttnArgs a, Workspace w) {
     __syncthreads();
     item = next;
     cur = nxt;
-    qpos += q_wgs;
+    ++rnd;
   }
   if (blk_bad && lane == 0) atomicOr(&w.hdr[H_FLAGS], PA_FLAG_BLOCK_ID);
 }

@@ -131,9 +131,16 @@ __device__ __forceinline__ int4 cut_record(int64_t f, int64_t pages, int64_t per
 // itself, without the plan kernel; also the most sequences of a step the chunk
 // kernel plans by itself.
 constexpr int kSelfPlanRows = 512;
-// Most query tokens of a step the chunk kernel plans by itself (its tiles then
-// run in sequence order, not longest first).
+// Most query tokens of a step the chunk kernel plans by itself in any case.
 constexpr int kChunkSelfPlanTokens = 2048;
+// A self-planned step whose tiles the chunk kernel can also put longest first
+// (it ranks every tile against every sequence in LDS): at most this many
+// sequences, tiles (an upper bound: tokens / tile rows + sequences) and
+// tile-sequence pairs.  Such a step self-plans at any size when every sequence
+// goes to the chunk kernel.
+constexpr int kChunkSortSeqs = 64;
+constexpr int kChunkSortTiles = 1024;
+constexpr int kChunkSortPairs = 16384;
 
 struct AttnArgs {
   const void* q;
@@ -159,7 +166,8 @@ struct AttnArgs {
   int32_t merge_rows;  // most query rows of one row-wise record this step (the plan's verify_rows)
   int32_t self_plan;   // 1: the MFMA decode kernel plans the step's row-wise rows by itself (no plan kernel)
   int32_t self_skip_chunks;  // with self_plan: sequences with more than one query row belong to the chunk kernel
-  int32_t chunk_self_plan;   // 1: small step the chunk kernel plans by itself (no plan kernel)
+  int32_t chunk_self_plan;   // the chunk kernel plans the step by itself (no plan kernel): 1 tiles in
+                             //   sequence order, 2 longest first
   int32_t all_chunk;         // 1: every sequence with query rows goes to the chunk kernel (the plan's all_chunk)
   int32_t fixed_units, num_ranges, max_len;  // the plan's range parameters, for self_plan
 };

@@ -121,6 +121,33 @@ def test_chunk_kernel_long_items_every_group(d, g):
     _check_attention(spec, ds, ds.attention())
 
 
+@pytest.mark.parametrize("case", ["ties sorted", "too many to sort", "all-chunk beyond 2048 sorted", "mixed sorted"])
+def test_self_planned_chunk_orders(case):
+    """Steps the chunk kernel plans by itself: tiles ranked longest first in
+    LDS (equal tiles by index) and taken in zigzag rounds when the items take
+    more than one round of the grid, or in sequence order when there are too
+    many sequences to rank (or one round); every tile is computed exactly once
+    either way."""
+    import math
+    if case == "ties sorted":            # 40 identical sequences: every key count tied 40 ways
+        reqs = [W.Request(i, 100, 70) for i in range(40)]
+    elif case == "too many to sort":     # 70 sequences > the ranking limit
+        reqs = [W.Request(i, 13 * i, 8) for i in range(70)]
+    elif case == "all-chunk beyond 2048 sorted":  # 4200 tokens, every sequence a chunk
+        reqs = [W.Request(i, [0, 64, 500, 1000, 33, 700][i], 700) for i in range(6)]
+    else:                                # chunks next to decodes, more items than one grid round
+        reqs = [W.Request(i, 17 * i, 40 if i < 40 else 1) for i in range(60)]
+    nb = sum(-(-r.seq_len // 16) for r in reqs) + 4
+    seed = 2400 + len(reqs)
+    order = np.random.default_rng(seed).permutation(nb).astype(np.int32)
+    spec = W.StepSpec(f"self-plan {case}", seed, 32, 8, 128, "bf16", 16, nb, 1.0 / math.sqrt(128.0), reqs,
+                      initial_order=order, table_rows=4096, seed=seed)
+    print(f"self-planned chunk order: {case}, {len(reqs)} sequences, {sum(r.query for r in reqs)} tokens", flush=True)
+    ds = build_device_step(spec)
+    ds.reshape()
+    _check_attention(spec, ds, ds.attention())
+
+
 @pytest.mark.parametrize("hkv,g", [(8, 4), (16, 2)])
 def test_chunk_kernel_xcd_queues(hkv, g):
     """Kv-head counts that split evenly over the per-XCD work queues (one or two
