@@ -377,6 +377,11 @@ def main(argv=None):
     # (kept out of the step timing above: the extra event records cost time)
     pk.pa_profile_enable((1 << pk.PA_K_COUNT) - 1)
     pk.pa_profile_read()
+    # a matrix-core loop of a few ms first, so that the host queues this pass
+    # ahead of the GPU: a short step would otherwise wait for the host between
+    # its launches, and the events around a kernel would count that wait
+    head = torch.empty(65536, dtype=torch.float32, device="cuda:0")
+    pk.pa_measure_mfma(max(40000, 2000 * args.steps), head)
     for i in range(args.steps):
         step(args.warmup + i)
     torch.cuda.synchronize()
