@@ -400,10 +400,18 @@ def main(argv=None):
     use_mfma = spec.dtype == "bf16" and pk.pa_get_option(pk.PA_OPT_FORCE_ROWWISE) == 0 and prof["chunk_mfma"][0] > 0
     g = spec.num_q_heads // spec.num_kv_heads
     vr_opt = pk.pa_get_option(pk.PA_OPT_VERIFY_ROWS)
-    # short queries go row-wise only when the option asks for it (the library's
-    # default sends them to the chunk kernel), capped at one 16-wide accumulator
-    verify = (1 if spec.dtype != "bf16" or pk.pa_get_option(pk.PA_OPT_DECODE_KERNEL) == 1
-              or pk.pa_get_option(pk.PA_OPT_FORCE_ROWWISE) or vr_opt < 1 else min(vr_opt, 16 // g))
+    # short queries go row-wise as records of up to 16 / G rows (one 16-wide
+    # accumulator): with the option, on every step; by default only on a step
+    # small enough for the row-wise kernel to plan by itself whose sequences all
+    # fit one record (the library's rule)
+    max_q = max(r.query for r in spec.requests)
+    if spec.dtype != "bf16" or pk.pa_get_option(pk.PA_OPT_DECODE_KERNEL) == 1 or pk.pa_get_option(
+            pk.PA_OPT_FORCE_ROWWISE):
+        verify = 1
+    elif vr_opt >= 1:
+        verify = min(vr_opt, 16 // g)
+    else:
+        verify = (16 // g if 2 <= max_q <= 16 // g and spec.num_tokens <= 512 and spec.num_seqs <= 512 else 1)
     work = algorithmic_work(spec, use_mfma, verify)
     ms = dt * 1e3 / n_steps
     decode_n, decode_ms = prof["decode"]

@@ -227,7 +227,11 @@ enum {
                                 query rows (a short query, e.g. speculative-decoding verification)
                                 is one row-wise work item whose rows share every K/V page instead
                                 of chunk tiles; n = this value capped at 16 / (q heads per kv
-                                head); 0 (automatic) and 1: off.  Changes the workspace size */
+                                head); 1: off; 0 (automatic): n = 16 / (q heads per kv head) on
+                                steps of at most 512 rows and sequences whose max_query_len is
+                                at most that (the row-wise kernel plans them by itself, no chunk
+                                kernel runs), off on other steps.  Values >= 2 change the
+                                workspace size */
   PA_OPT_CHUNK_KERNEL = 7    /* bf16 chunk rows: 0 (automatic) and 1: the four-wavefront chunk
                                 kernel; 2: the eight-wavefront kernel (two groups alternating
                                 products and softmax) for every step with chunk rows, the plan

@@ -100,8 +100,11 @@ int64_t ranges_capacity(const StepShape& s) {
 int verify_rows(int group) {
   const int cap = 16 / (group > 0 && group <= 16 ? group : 16);  // one 16-wide accumulator
   const int64_t v = option(PA_OPT_VERIFY_ROWS);
-  // automatic: off -- the chunk kernel measured faster on short queries
-  // (64 sequences x 2..4 rows over contexts of 512-2048: 86-89 us against 92-99 us)
+  // automatic: one row per record in the workspace layout.  run_attention
+  // still takes records of up to `cap` rows on steps the decode kernel plans
+  // by itself, in the same partial arrays (fewer, longer ranges); on planned
+  // steps the chunk kernel measured faster on short queries (64 sequences x
+  // 2..4 rows over contexts of 512-2048: 86-89 us against 92-99 us)
   if (v >= 1) return v < cap ? int(v) : cap;
   return 1;
 }
@@ -205,10 +208,33 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   const int group = num_q_heads / num_kv_heads;
   StepShape shape{num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq};
 
-  const Workspace w = layout_workspace(shape, workspace);
+  Workspace w = layout_workspace(shape, workspace);
   const bool bf16 = dtype == PA_BF16;
+  // short queries share their pages in one record: only the MFMA decode kernel
+  // has the per-column causal limits (and the debug route keeps one row per record)
+  const bool vr_auto = option(PA_OPT_VERIFY_ROWS) == 0;
+  int vrows = bf16 && max_query_len > 1 && decode_uses_mfma(1) && !option(PA_OPT_FORCE_ROWWISE)
+                  ? (vr_auto ? 16 / group : verify_rows(group))
+                  : 1;
+  // a small step whose sequences all fit one record each (by the hint): the
+  // decode kernel plans it by itself, as records, and no chunk kernel runs (a
+  // sequence longer than the hint says becomes several records)
+  const bool self_records =
+      vrows >= 2 && max_query_len <= vrows && num_tokens <= kSelfPlanRows && num_seqs <= kSelfPlanRows;
+  if (vr_auto) {
+    if (!self_records) {
+      vrows = 1;  // automatic: records only where the decode kernel plans them itself
+    } else {
+      // the workspace was laid out for one-row records (G columns per partial
+      // slot); the same partial arrays hold fewer ranges of G * vrows columns
+      // (a self-planned step lengthens its ranges to fit)
+      w.ranges_cap = w.ranges_cap * w.ncol / (int64_t(group) * vrows);
+      w.ncol = group * vrows;
+    }
+  }
   // a decode-only step (every query of length <= 1) has no chunk tiles
-  const bool use_mfma = !option(PA_OPT_FORCE_ROWWISE) && max_query_len > 1 && chunk_supported(head_dim, group, bf16);
+  const bool use_mfma = !option(PA_OPT_FORCE_ROWWISE) && max_query_len > 1 && !self_records &&
+                        chunk_supported(head_dim, group, bf16);
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   PlanArgs pa_args{};
@@ -227,10 +253,7 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
     pa_args.num_ranges = int32_t(n < 1 ? 1 : n);
   }
   pa_args.tile_rows = use_mfma ? chunk_tile_rows(group) : 1;
-  // short queries share their pages in one record: only the MFMA decode kernel
-  // has the per-column causal limits (and the debug route keeps one row per record)
-  pa_args.verify_rows =
-      bf16 && max_query_len > 1 && decode_uses_mfma(1) && !option(PA_OPT_FORCE_ROWWISE) ? verify_rows(group) : 1;
+  pa_args.verify_rows = vrows;
   // T = S * max_query_len: with a true hint every sequence has max_query_len rows, too many
   // for a row-wise record, so no row-wise row exists and the decode and merge kernels are not
   // launched.  The plan then sends every sequence to the chunk kernel, so a wrong hint (some
@@ -271,9 +294,11 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   a.bf16 = bf16 ? 1 : 0;
   a.merge_rows = pa_args.verify_rows;
   // a small decode-only step on the MFMA decode kernel skips the plan kernel:
-  // every decode workgroup plans the (few) rows itself
-  a.self_plan = max_query_len <= 1 && bf16 && decode_uses_mfma(1) && num_tokens <= kSelfPlanRows &&
-                num_seqs <= kSelfPlanRows;
+  // every decode workgroup plans the (few) rows itself; so does a small step
+  // of short-query records
+  a.self_plan = (max_query_len <= 1 && bf16 && decode_uses_mfma(1) && num_tokens <= kSelfPlanRows &&
+                 num_seqs <= kSelfPlanRows) ||
+                self_records;
   // a small step with chunks skips it too: the chunk kernel plans its tiles and
   // the MFMA decode kernel the single-row sequences (short-query records need
   // the plan kernel)

@@ -157,7 +157,10 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
   // instead of by the plan kernel: the row records and their first units go
   // to LDS (workgroup 0 also stores them, and the step's header, for the
   // merge), and each range finds its first row by binary search.  Same
-  // records, units and ranges as the plan kernel's.
+  // records, units and ranges as the plan kernel's (records of up to
+  // merge_rows rows on a short-query step; a sequence with more rows than
+  // that, which the plan would give the chunk kernel, becomes several records
+  // here).
   __shared__ int4 s_rec[SELF ? kSelfPlanRows : 1];
   __shared__ int64_t s_base[SELF ? kSelfPlanRows : 1];
   __shared__ int64_t s_tot[2 * kWaves];
@@ -165,6 +168,7 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
   if constexpr (SELF) {
     const int tid = threadIdx.x;
     const int64_t hkv = a.hkv;
+    const int vr = a.merge_rows;  // most query rows of one record (1: one record per row)
     constexpr int SPT = kSelfPlanRows / kThreads;  // sequences per thread
     int32_t r0s[SPT], qs[SPT], cs[SPT];
     int64_t nr = 0, nu = 0;
@@ -187,8 +191,15 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
       r0s[k] = r0;
       qs[k] = q;
       cs[k] = c;
-      nr += q;
-      nu += hkv * (pages_upto(int64_t(c) + q) - pages_upto(c));
+      if (vr <= 1) {  // one record per row: rows c+1 .. c+q keys
+        nr += q;
+        nu += hkv * (pages_upto(int64_t(c) + q) - pages_upto(c));
+      } else {  // records of up to vr consecutive rows, each over its last row's keys
+        for (int32_t j = 0; j < q; j += vr) {
+          ++nr;
+          nu += hkv * ((int64_t(c) + min(q, j + vr) + kBlock - 1) / kBlock);
+        }
+      }
     }
     // exclusive scans of (rows, units) over the workgroup
     int64_t ir = nr, iu = nu;
@@ -216,9 +227,11 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
     int64_t r = br + ir - nr, u = bu + iu - nu;
 #pragma unroll
     for (int k = 0; k < SPT; ++k) {
-      for (int32_t j = 0; j < qs[k] && r < kSelfPlanRows; ++j, ++r) {
-        const int32_t len = cs[k] + j + 1;
-        s_rec[r] = make_int4(r0s[k] + j, tid * SPT + k, len, 1);
+      const int step = vr > 1 ? vr : 1;
+      for (int32_t j = 0; j < qs[k] && r < kSelfPlanRows; j += step, ++r) {
+        const int32_t nq = min(step, qs[k] - j);  // the record's rows j .. j + nq - 1
+        const int32_t len = cs[k] + j + nq;       // keys its last row sees
+        s_rec[r] = make_int4(r0s[k] + j, tid * SPT + k, len, nq);
         s_base[r] = u;
         u += hkv * ((len + kBlock - 1) / kBlock);
       }
@@ -281,12 +294,12 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
   // issued while the current pair's last page is multiplied.  Inside the
   // loop only the page copies are loads in flight and LDS is touched only by
   // the copies and the V operand reads, so the compiler's own waits stay
-  // per page.  (The records are in LDS; a decode record has one query row.)
+  // per page.  (The records are in LDS; a decode record has one query row, a
+  // short query's up to 16 / G.)
   auto flat_range = [&](int g, int64_t x, int64_t x_end, int r, int kvh, int p0) __attribute__((always_inline)) {
     if constexpr (SELF) {
       const int hkv = a.hkv;
       const int total = int(x_end - x);
-      const bool col_ok = jrow < 1;
       // (record fields are wave-uniform: read them into scalars)
       auto pages_of = [&](int rr) __attribute__((always_inline)) {
         return __builtin_amdgcn_readfirstlane((s_rec[rr].z + kBlock - 1) / kBlock);
@@ -297,12 +310,15 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
           ++rr;
         }
       };
-      // Q of pair (rr, kh) as the B operand: lane holds head hq (zeros past the group), dims 8grp + 32kk
+      // Q of pair (rr, kh) as the B operand: lane holds row jrow, head hh of the
+      // record (zeros past its rows), dims 8grp + 32kk
       auto load_q = [&](int rr, int kh, u32x4 (&qq)[KS]) __attribute__((always_inline)) {
+        const bool ok = jrow < __builtin_amdgcn_readfirstlane(s_rec[rr].w);
+        const int tok = __builtin_amdgcn_readfirstlane(s_rec[rr].x) + (ok ? jrow : 0);
         const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) +
-                                                         (int64_t(s_rec[rr].x) * a.hq + int64_t(kh) * G + hh) * RB);
+                                                         (int64_t(tok) * a.hq + int64_t(kh) * G + hh) * RB);
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) qq[kk] = col_ok ? qp[grp + 4 * kk] : u32x4{0u, 0u, 0u, 0u};
+        for (int kk = 0; kk < KS; ++kk) qq[kk] = ok ? qp[grp + 4 * kk] : u32x4{0u, 0u, 0u, 0u};
       };
 
       // page table of the stream, 64 pages at a time: lane j holds the block id
@@ -372,7 +388,8 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
 
       // compute side: pair (cr, ckh) (the range's pair number cn), page cp; this range's part of it began at cp0
       int cr = r, ckh = kvh, cn = 0, cp = p0, cp0 = p0, cleft = total, cpages = pages_of(r);
-      int clen = __builtin_amdgcn_readfirstlane(s_rec[r].z);
+      int clen = __builtin_amdgcn_readfirstlane(s_rec[r].z);  // keys the record's last row sees
+      int cnq = __builtin_amdgcn_readfirstlane(s_rec[r].w);   // the record's rows
       u32x4 qf[KS];
       f32x4_t o[DB];
 #pragma unroll
@@ -402,8 +419,8 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
         for (int kk = 0; kk < KS; ++kk)
           sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]),
                                                       __builtin_bit_cast(bf16x8_t, qf[kk]), sc, 0, 0, 0);
-        const int kfirst = pos0 + 4 * grp;  // key of accumulator row 0 of this lane
-        const int lim = clen + jrow;        // keys this column's row sees
+        const int kfirst = pos0 + 4 * grp;   // key of accumulator row 0 of this lane
+        const int lim = clen - cnq + 1 + jrow;  // keys this column's row sees
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[i] = kfirst + i < lim ? sc[i] * a.scale_log2 : -INFINITY;
         float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -430,10 +447,10 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
           lt += __shfl_xor(lt, 32);
           const bool whole = cp0 == 0 && cp == cpages;
           const int64_t slot = int64_t(g) * 2 + (cn == 0 ? 0 : 1);
-          if (col_ok) {
+          if (jrow < cnq) {
             if (whole) {
               const float inv = 1.f / lt;
-              float* op = a.out + (int64_t(s_rec[cr].x) * a.hq + int64_t(ckh) * G + hh) * D + 4 * grp;
+              float* op = a.out + (int64_t(s_rec[cr].x + jrow) * a.hq + int64_t(ckh) * G + hh) * D + 4 * grp;
 #pragma unroll
               for (int db = 0; db < DB; ++db)
                 store_f4(op + 16 * db, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
@@ -452,6 +469,7 @@ decode_mfma_kernel(AttnArgs a, Workspace w) {
             cp0 = 0;
             cpages = pages_of(cr);
             clen = __builtin_amdgcn_readfirstlane(s_rec[cr].z);
+            cnq = __builtin_amdgcn_readfirstlane(s_rec[cr].w);
 #pragma unroll
             for (int db = 0; db < DB; ++db) o[db] = f32x4_t{};
             m = -INFINITY;

@@ -30,8 +30,10 @@ TOL = 1e-2  # bf16 inputs, fp32 accumulation
 @pytest.fixture(autouse=True)
 def _chunk_pp():
     pk.pa_set_option(pk.PA_OPT_CHUNK_KERNEL, 2)
+    pk.pa_set_option(pk.PA_OPT_VERIFY_ROWS, 1)  # short queries stay chunk rows too
     yield
     pk.pa_set_option(pk.PA_OPT_CHUNK_KERNEL, 0)
+    pk.pa_set_option(pk.PA_OPT_VERIFY_ROWS, 0)
     pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, 0)
 
 

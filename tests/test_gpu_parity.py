@@ -269,6 +269,58 @@ def test_short_queries_share_pages(seed):
             _check_attention(spec, ds, ds.attention())
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_self_planned_short_query_records(seed):
+    """Small steps whose sequences all have at most 16 / G query rows (speculative-
+    decoding verification), records on: the MFMA decode kernel plans the records by
+    itself (no plan or chunk kernel) -- contexts from 0 to a few thousand tokens,
+    every group size and head size, ranges that cut records.  Then the same step with
+    a max_query_len hint below the longest sequences' rows: those become several
+    records each (or, past the self-planned size, take the planned path)."""
+    import math
+    r = np.random.default_rng((seed, 11))
+    g = [1, 2, 4, 8][seed % 4]
+    hkv = [2, 1][(seed // 4) % 2]
+    d = [64, 128][(seed // 2) % 2]
+    cap = 16 // g
+    for case in ("fits", "hint too low"):
+        n = int(r.integers(8, 64))
+        hi = cap if case == "fits" else 3 * cap
+        n = min(n, 500 // hi)
+        ctx = np.where(r.random(n) < 0.3, r.integers(0, 40, n), r.integers(40, 3000, n))
+        qs = r.integers(1, hi + 1, n)
+        if case == "hint too low":
+            qs[0] = hi  # at least one sequence longer than the hint
+        reqs = [W.Request(i, int(c), int(q)) for i, (c, q) in enumerate(zip(ctx, qs))]
+        nb = sum(-(-(int(c) + int(q)) // 16) for c, q in zip(ctx, qs)) + 4
+        order = np.random.default_rng((seed, 12)).permutation(nb).astype(np.int32)
+        spec = W.StepSpec(f"short-query records {case}", 3100 + seed, hkv * g, hkv, d, "bf16", 16, nb,
+                          1.0 / math.sqrt(d), reqs, initial_order=order, table_rows=2048, seed=3100 + seed)
+        print(f"short-query records seed={seed} case={case} g={g} hkv={hkv} d={d} seqs={n} "
+              f"tokens={spec.num_tokens} max_q={int(qs.max())}", flush=True)
+        ds = build_device_step(spec)
+        ds.reshape()
+        pk.pa_set_option(pk.PA_OPT_VERIFY_ROWS, 16)
+        for split in (0, 16, 256):
+            pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, split)
+            if case == "fits":
+                out = ds.attention()
+            else:
+                out = pk.pa_attention(ds.q, ds.k_cache, ds.v_cache, ds.block_tables, ds.seq_lens,
+                                      ds.query_start_loc, ds.context_lens, spec.scale, max_query_len=cap)
+            _check_attention(spec, ds, out)
+
+
+def test_short_query_configuration_as_records():
+    """The short-query configuration (64 sequences x 4 query rows over contexts of
+    512-2048, GQA 4:1) with records on, every row against the oracle."""
+    spec = W.make_config(6)
+    ds = build_device_step(spec)
+    ds.reshape()
+    pk.pa_set_option(pk.PA_OPT_VERIFY_ROWS, 4)
+    _check_attention(spec, ds, ds.attention())
+
+
 def test_max_query_len_hint_never_changes_results():
     """<= 1 sends every row to the row-wise kernel: exact for a decode step,
     within tolerance (other kernel) for a mixed step given a wrong hint; a hint
