@@ -83,6 +83,26 @@ def algorithmic_work(spec, mfma_rows: bool, verify_rows: int = 1):
                 reshape_bytes=spec.num_tokens * (2 * kv_tok + 4))
 
 
+def step_roofline(work, mfma_rows: bool, ms: float, ceil=None):
+    """The whole step against its roofline: T_roof = (row-wise kernel bytes + chunk
+    kernel bytes) / HBM bandwidth + chunk flops / matrix-core peak, each kernel class at its
+    own bound, summed (the classes run one after the other); frac = T_roof / T_measured.
+    Against the spec figures, and against the ceilings measured in the same run (random
+    4 KiB page gather, matrix-core loop on N(0,1)-like operands) when there are any."""
+    def t_roof(bw_gbs, mfma_tflops):
+        t = work["decode_kernel_bytes"] / (bw_gbs * 1e9)
+        if mfma_rows and work["chunk_flops"] > 0:
+            t += max(work["chunk_kernel_bytes"] / (bw_gbs * 1e9), work["chunk_flops"] / (mfma_tflops * 1e12))
+        return t * 1e3
+    spec_ms = t_roof(HBM_PEAK_GBS, MFMA_BF16_PEAK_TFLOPS)
+    out = {"t_roof_ms": spec_ms, "t_step_ms": ms, "frac": spec_ms / ms}
+    if ceil:
+        meas_ms = t_roof(ceil["gather4k_GBps"], ceil["mfma_bf16_random_TFLOPs"])
+        out["t_roof_measured_ms"] = meas_ms
+        out["frac_of_measured"] = meas_ms / ms
+    return out
+
+
 def measure_ceilings(pk, torch, reps: int = 10):
     """Measured ceilings on this device: streaming copy of 4 GiB (read + write
     bytes), a read-only pass over 8 GiB, a gather of its 4 KiB pages in random
@@ -480,6 +500,7 @@ def main(argv=None):
         "launch": (f"hip_graph ({per_launch} step{'s' if per_launch > 1 else ''} per replay)" if args.graph
                    else "stream"),
         "host_issue_us_per_step": t_issue * 1e6 / n_steps,
+        "step_roofline": step_roofline(work, use_mfma, ms, ceil),
         "ceilings": ceil,
     }
     if not args.no_cpu_baseline:

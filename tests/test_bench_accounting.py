@@ -94,3 +94,22 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def test_step_roofline_sums_kernel_classes_at_their_bounds():
+    """The whole-step roofline: row-wise bytes over HBM plus, for the chunk rows, the
+    larger of their bytes over HBM and their flops over the matrix cores.  On the
+    chunked-prefill configuration (no row-wise rows) that is 68 753 031 168 flops at
+    2.5 PFLOP/s = 27.5 us; on a decode-only step it is the bytes over 8 TB/s."""
+    w3 = bench.algorithmic_work(W.make_config(3), mfma_rows=True)
+    r3 = bench.step_roofline(w3, True, 0.110)
+    assert w3["decode_kernel_bytes"] == 0
+    assert abs(r3["t_roof_ms"] - 68_753_031_168 / 2.5e15 * 1e3) < 1e-12
+    assert abs(r3["frac"] - r3["t_roof_ms"] / 0.110) < 1e-15
+    w2 = bench.algorithmic_work(W.make_config(2), mfma_rows=False)
+    r2 = bench.step_roofline(w2, False, 0.066, {"gather4k_GBps": 6600.0, "mfma_bf16_random_TFLOPs": 1850.0})
+    assert abs(r2["t_roof_ms"] - w2["decode_kernel_bytes"] / 8e12 * 1e3) < 1e-12
+    assert abs(r2["t_roof_measured_ms"] - w2["decode_kernel_bytes"] / 6.6e12 * 1e3) < 1e-12
+    work = {"decode_kernel_bytes": 8e9, "chunk_kernel_bytes": 1e9, "chunk_flops": 5e12}
+    r = bench.step_roofline(work, True, 2.0)
+    assert abs(r["t_roof_ms"] - (1.0 + 2.0)) < 1e-12  # 8 GB at 8 TB/s, then 5 TFLOP at 2.5 PFLOP/s
