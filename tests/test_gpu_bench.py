@@ -40,3 +40,6 @@ def test_bench_prints_one_json_line(cfg, bound, unit):
     assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"])
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0 and cpu["sample"]
+    step = d["step_roofline"]
+    assert step["t_step_ms"] == pytest.approx(d["ms_per_step"])
+    assert 0 < step["frac"] == pytest.approx(step["t_roof_ms"] / step["t_step_ms"])
