@@ -150,3 +150,15 @@ def test_noalloc_attention_rejects_bad_arguments_and_oversized_steps():
     assert pk.pa_attention_workspace_size(1, big_T, 8, 1, 128, 8) > (96 << 20)
     assert call(hq=8, hkv=1, S=1, T=big_T, mbps=8) == pk.PA_ERR_WORKSPACE
     assert "static scratch" in pk.last_error()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libpa.so the binding raises at the first call: there is no CPU
+    or PyTorch fallback for any step of the path."""
+    from paged_kv_varlen_reshape_amd import _binding
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "libpa.so"))
+    monkeypatch.setattr(_binding, "_lib", None)
+    with pytest.raises(ImportError, match="no fallback"):
+        _binding.lib()
+    with pytest.raises(ImportError):
+        _binding.pa_attention_workspace_size(64, 64, 32, 8, 128, 129)
