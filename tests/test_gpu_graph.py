@@ -23,6 +23,7 @@ TOL = {"f32": 1e-5, "bf16": 1e-2}
 def _specs():
     yield "decode bf16", W.make_config(2)
     yield "chunked prefill bf16", W.make_config(3)
+    yield "short queries bf16", W.make_config(6)  # self-planned multi-row records
     yield "mixed f32", W.random_spec(50, num_seqs=6, max_context=200, max_query=30, num_q_heads=8, num_kv_heads=2,
                                      head_dim=64, dtype="f32", prefix_tokens=16, decode_fraction=0.5)
     yield "mixed bf16", W.random_spec(51, num_seqs=7, max_context=300, max_query=40, num_q_heads=16,
