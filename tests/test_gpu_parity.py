@@ -300,15 +300,18 @@ def test_self_planned_short_query_records(seed):
               f"tokens={spec.num_tokens} max_q={int(qs.max())}", flush=True)
         ds = build_device_step(spec)
         ds.reshape()
-        pk.pa_set_option(pk.PA_OPT_VERIFY_ROWS, 16)
-        for split in (0, 16, 256):
-            pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, split)
-            if case == "fits":
-                out = ds.attention()
-            else:
-                out = pk.pa_attention(ds.q, ds.k_cache, ds.v_cache, ds.block_tables, ds.seq_lens,
-                                      ds.query_start_loc, ds.context_lens, spec.scale, max_query_len=cap)
-            _check_attention(spec, ds, out)
+        # 0: automatic (records in the one-row workspace layout, fewer and longer
+        # ranges); 16: on request (the cap, a workspace laid out for it)
+        for vr in (0, 16):
+            pk.pa_set_option(pk.PA_OPT_VERIFY_ROWS, vr)
+            for split in (0, 16, 256):
+                pk.pa_set_option(pk.PA_OPT_SPLIT_TOKENS, split)
+                if case == "fits":
+                    out = ds.attention()
+                else:
+                    out = pk.pa_attention(ds.q, ds.k_cache, ds.v_cache, ds.block_tables, ds.seq_lens,
+                                          ds.query_start_loc, ds.context_lens, spec.scale, max_query_len=cap)
+                _check_attention(spec, ds, out)
 
 
 def test_short_query_configuration_as_records():
