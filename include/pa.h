@@ -130,7 +130,11 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t
  *   out              [num_tokens, num_q_heads, head_dim] float32
  *   max_query_len    (host) the longest query of the step, as a scheduler
  *                    knows it.  <= 1 routes every row to the row-wise kernel
- *                    and skips the chunk kernel's launch; > 1 with
+ *                    and skips the chunk kernel's launch; 2 .. 16 /
+ *                    (q heads per kv head) on a bf16 step of at most 512
+ *                    rows and sequences makes every sequence row-wise
+ *                    records of up to that many rows (PA_OPT_VERIFY_ROWS
+ *                    automatic) and skips the plan and chunk kernels; > 1 with
  *                    num_tokens == num_seqs * max_query_len (every sequence
  *                    that long) routes every row to the chunk kernel and skips
  *                    the row-wise kernels' launches.  A wrong value changes
