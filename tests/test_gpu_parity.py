@@ -462,3 +462,43 @@ def test_full_size_configs_sampled(cfg):
         assert torch.equal(got.view(torch.int16), new.view(torch.int16))
     del ds
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("block", range(4))
+def test_random_steps_under_random_options(block):
+    """Seeded random steps (1-600 sequences, contexts up to 3000, queries up to
+    300 rows, decode fractions 0-1, shared prefixes, every group size, kv-head
+    count and head size, bf16 and fp32) under random option combinations
+    (records automatic / off / on request, the eight-wavefront chunk kernel,
+    split lengths, forced row-wise, the VALU decode kernel) and max_query_len
+    hints that are right or wrong: sampled sequences against the oracle."""
+    for c in range(10):
+        seed = 9000 + 10 * block + c
+        r = np.random.default_rng(seed)
+        g = int(r.choice([1, 2, 4, 8]))
+        hkv = int(r.choice([1, 2, 4, 8]))
+        d = int(r.choice([64, 128]))
+        dtype = "bf16" if r.random() < 0.8 else "f32"
+        n = int(r.choice([1, 3, 17, 64, 200, 600]))
+        spec = W.random_spec(seed, num_seqs=n, max_context=int(r.choice([1, 30, 300, 3000])),
+                             max_query=int(r.choice([1, 2, 4, 9, 40, 300])), num_q_heads=hkv * g,
+                             num_kv_heads=hkv, head_dim=d, dtype=dtype, prefix_tokens=int(r.choice([0, 16, 48])),
+                             decode_fraction=float(r.choice([0.0, 0.5, 0.9, 1.0])))
+        opts = {pk.PA_OPT_VERIFY_ROWS: int(r.choice([0, 0, 1, 16])), pk.PA_OPT_CHUNK_KERNEL: int(r.choice([0, 0, 0, 2])),
+                pk.PA_OPT_SPLIT_TOKENS: int(r.choice([0, 0, 16, 48])), pk.PA_OPT_FORCE_ROWWISE: int(r.random() < 0.1),
+                pk.PA_OPT_DECODE_KERNEL: int(r.random() < 0.15)}
+        for k, v in opts.items():
+            pk.pa_set_option(k, v)
+        ds = build_device_step(spec)
+        ds.reshape()
+        hint = ds.max_query_len if r.random() < 0.8 else int(r.choice([1, 2, 4, spec.num_tokens]))
+        print(f"random step seed={seed} {dtype} g={g} hkv={hkv} d={d} seqs={n} tokens={spec.num_tokens} "
+              f"hint={hint} options={list(opts.values())}", flush=True)
+        out = pk.pa_attention(ds.q, ds.k_cache, ds.v_cache, ds.block_tables, ds.seq_lens, ds.query_start_loc,
+                              ds.context_lens, spec.scale, max_query_len=hint)
+        seqs = sorted(r.choice(spec.num_seqs, min(spec.num_seqs, 24), replace=False).tolist())
+        _check_attention(spec, ds, out, seqs)
+        for k in opts:
+            pk.pa_set_option(k, 0)
+        del ds, out
+        torch.cuda.empty_cache()
