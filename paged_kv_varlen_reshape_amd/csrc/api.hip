@@ -71,11 +71,6 @@ namespace {
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Most (sequence, block-table entry, kv head) pages a decode-only step may name
-// and still be planned by the decode kernel itself (about 4096 pages per range
-// at the usual 1024 ranges).
-constexpr int64_t kSelfPlanPagesBound = int64_t(1) << 22;
-
 int check_dims(int32_t hkv, int32_t d, int32_t bs, int32_t dtype, int64_t nb, const char* who) {
   if (hkv <= 0 || hkv >= (1 << 15)) return fail(PA_ERR_INVALID, "%s: num_kv_heads %d out of range", who, hkv);
   if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d not supported", who, dtype);
@@ -300,14 +295,9 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, const
   a.merge_rows = pa_args.verify_rows;
   // a small decode-only step on the MFMA decode kernel skips the plan kernel:
   // every decode workgroup plans the (few) rows itself; so does a small step
-  // of short-query records.  Not when the step may hold long contexts (its
-  // pages could reach thousands per range): there the planned kernel, which
-  // copies V pages into LDS instead of passing them through registers, streams
-  // about 1 % faster, more than the plan kernel costs (long-context step with
-  // a shared prefix: 3664-3684 against 3700-3708 us)
-  const bool long_ranges = int64_t(num_seqs) * max_blocks_per_seq * num_kv_heads > kSelfPlanPagesBound;
+  // of short-query records
   a.self_plan = (max_query_len <= 1 && bf16 && decode_uses_mfma(1) && num_tokens <= kSelfPlanRows &&
-                 num_seqs <= kSelfPlanRows && !long_ranges) ||
+                 num_seqs <= kSelfPlanRows) ||
                 self_records;
   // a small step with chunks skips it too: the chunk kernel plans its tiles and
   // the MFMA decode kernel the single-row sequences (short-query records need
